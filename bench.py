@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MXFP4 GEMM (A bf16 quantized on the fly) on one MI355X.
+
+A step is one call of the whole per-call path -- quantize A in registers,
+multiply by the preshuffled MXFP4 B, reduce, store bf16 C -- over one batch of
+synthetic input.  B is prepared once, outside the timed region, by the
+library's own quantize and preshuffle kernels.
+
+Timing: K steps are captured into one HIP graph and replayed; the timed
+region is that replay, bracketed by device synchronizations, with HIP events
+recorded on the replay stream.  In the default "cold" mode consecutive steps
+cycle through enough copies of (A, B, scales, C) -- at least 1 GiB -- that
+each step's inputs come from HBM rather than L2 or the 256 MB MALL.
+
+Prints one JSON line.  The headline workload is M=32, N=4096, K=512; the
+line also carries every measured configuration under "per_config".
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 matrix peak, TFLOP/s
+HEADLINE = "c2"
+
+
+def alg_bytes(M, N, K):
+    """A bf16 + B e2m1 + B e8m0 + C bf16, each counted once."""
+    return 2 * M * K + N * K // 2 + N * K // 32 + 2 * M * N
+
+
+def alg_flops(M, N, K):
+    return 2 * M * N * K
+
+
+def prepare(torch, mx, w, sets):
+    import numpy as np
+    dev = torch.device("cuda", 0)
+    a = torch.from_numpy(w.a_bits().view(np.int16)).view(torch.bfloat16).to(dev)
+    b = torch.from_numpy(w.b_bits().view(np.int16)).view(torch.bfloat16).to(dev)
+    qb, sb = mx.quantize(b)
+    bw, bs = mx.preshuffle_b(qb, sb)
+    del b, qb, sb
+    out = []
+    for i in range(sets):
+        if i == 0:
+            out.append((a, bw, bs, torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)))
+        else:
+            out.append((a.clone(), bw.clone(), bs.clone(), torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)))
+    torch.cuda.synchronize()
+    return out
+
+
+def time_config(torch, mx, w, steps, warmup, cold):
+    M, N, K = w.M, w.N, w.K
+    per_set = alg_bytes(M, N, K) + N * K // 32
+    sets = min(512, max(2, math.ceil((1 << 30) / per_set))) if cold else 1
+    bufs = prepare(torch, mx, w, sets)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        mx.mxfp4_reserve(M, N, K, stream=stream)
+        for i in range(warmup):
+            A, Bw, Bs, C = bufs[i % sets]
+            mx.mxfp4_gemm(A, Bw, Bs, C, M, N, K, stream=stream)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            A, Bw, Bs, C = bufs[i % sets]
+            mx.mxfp4_gemm(A, Bw, Bs, C, M, N, K, stream=stream)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g.replay()  # first replay uploads the graph
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = ev0.elapsed_time(ev1) / steps
+    del g, bufs
+    torch.cuda.empty_cache()
+    us = kern_ms * 1e3
+    return {
+        "M": M, "N": N, "K": K,
+        "schedule": mx.mxfp4_gemm_schedule_name(M, N, K),
+        "buffer_sets": sets,
+        "us_per_call": round(us, 4),
+        "wall_ms_per_step": wall * 1e3 / steps,
+        "tflops": alg_flops(M, N, K) / (us * 1e-6) / 1e12,
+        "alg_gbs": alg_bytes(M, N, K) / (us * 1e-6) / 1e9,
+        "hbm_frac": alg_bytes(M, N, K) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "mfma_frac": alg_flops(M, N, K) / (us * 1e-6) / 1e12 / FP4_PEAK_TFLOPS,
+    }
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle as it stands, single-threaded, on whole calls of the
+    headline workload (quantize A, exact GEMM, round) until the budget is
+    spent."""
+    import oracle
+    qb, sb = oracle.quantize(w.b_bits())
+    a = w.a_bits()
+    oracle.mxfp4_gemm_bf16(a, qb, sb)  # load + page in
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.mxfp4_gemm_bf16(a, qb, sb)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": alg_flops(w.M, w.N, w.K) * n / el / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": "%d whole calls of %s (quantize A + fp64 GEMM + bf16 rounding), %.1f s" % (n, w.name, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--configs", default="c1,c2,c3,c4,c5", help="configurations measured under per_config")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm", action="store_true", help="also time with one buffer set (caches warm)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this operation is built and timed on a single MI355X "
+              "(N-sharding of B across GPUs needs no collective and is not implemented); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(1)
+
+    import torch
+    import block_scaled_mxfp4_bf16_amd as mx
+    import synthetic as syn
+
+    torch.cuda.set_device(0)
+    names = [c for c in args.configs.split(",") if c]
+    if HEADLINE not in names:
+        names.insert(0, HEADLINE)
+    per = {}
+    for name in names:
+        w = syn.CONFIGS[name]
+        r = time_config(torch, mx, w, args.steps, args.warmup, cold=True)
+        if args.warm:
+            r["warm_us_per_call"] = time_config(torch, mx, w, args.steps, args.warmup, cold=False)["us_per_call"]
+        per[w.name] = r
+        print("[bench] %s: %.3f us/call cold, %.1f TFLOP/s, %.0f GB/s (%.1f%% of HBM), schedule %s"
+              % (w.name, r["us_per_call"], r["tflops"], r["alg_gbs"], 100 * r["hbm_frac"], r["schedule"]),
+              file=sys.stderr, flush=True)
+
+    hw = syn.CONFIGS[HEADLINE]
+    h = per[hw.name]
+    line = {
+        "metric": "us/call and TFLOPS per (M,N,K); % of HBM or MXFP4-MFMA roofline",
+        "value": h["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": h["wall_ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4 (e2m1 x e2m1 scaled MFMA, f32 accumulate, bf16 out)",
+        "data": "synthetic (Philox-4x32-10 + Box-Muller N(0,1) bf16, seeded)",
+        "config": {"workload": hw.name, "M": hw.M, "N": hw.N, "K": hw.K,
+                   "cache": "cold: %d rotating buffer sets" % h["buffer_sets"], "schedule": h["schedule"]},
+        "us_per_call": h["us_per_call"],
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(h["alg_gbs"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(h["hbm_frac"], 4),
+            "traffic": None,
+        },
+        "per_config": per,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(hw)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,278 @@
+// C ABI of libmxfp4.so: argument checks, schedule choice, the library-owned
+// split-K workspace, and the launches.  Every check runs on the host before
+// anything is enqueued.
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/mxfp4.h"
+#include "mxfp4_internal.hpp"
+
+using namespace mxfp4;
+
+namespace {
+
+const int64_t kMaxBytes = (int64_t)1 << 31;  // 32-bit offsets inside the kernels
+
+inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline int64_t pad_to(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// Process-wide options (testing and fallback).
+int g_quant_mode = 0;  // 0: hardware convert, 1: software encoder
+std::mutex g_opt_mu;
+std::string g_schedule_override;
+bool g_schedule_override_set = false;
+
+// Schedule choice.  The workgroup covers all of M when M <= 64 so every B
+// byte is fetched once; K is split so that roughly 256-512 workgroups exist.
+bool pick_schedule(int M, int N, int K, Schedule *out) {
+  Schedule s;
+  s.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  s.nt = 2;
+  s.waves = 4;
+  const int m_tiles = (M + 16 * s.mt - 1) / (16 * s.mt);
+  const int n_tiles = N / (16 * s.nt);
+  const int ks = (K + 127) / 128;
+  const int base = m_tiles * n_tiles;
+  int split = 1;
+  if (base < 256 && base <= kMaxSplitTiles) {
+    split = (512 + base - 1) / base;
+    int max_split = (ks + s.waves - 1) / s.waves;
+    if (split > max_split) split = max_split;
+    if (split < 1) split = 1;
+  }
+  static const int kpws[] = {1, 2, 4, 8};
+  for (;;) {
+    int need = (ks + split * s.waves - 1) / (split * s.waves);
+    int kpw = -1;
+    for (int k : kpws)
+      if (k >= need) {
+        kpw = k;
+        break;
+      }
+    if (kpw > 0) {
+      s.kpw = kpw;
+      break;
+    }
+    if (base > kMaxSplitTiles) return false;
+    ++split;
+  }
+  s.split = split;
+  s.variant = find_gemm_variant(s.mt, s.nt, s.kpw, s.waves);
+  if (s.variant < 0) return false;
+  *out = s;
+  return true;
+}
+
+// "mt1_nt2_kpw4_w4_split2"
+bool parse_schedule(const std::string &name, int M, int N, int K, Schedule *out) {
+  Schedule s;
+  if (sscanf(name.c_str(), "mt%d_nt%d_kpw%d_w%d_split%d", &s.mt, &s.nt, &s.kpw, &s.waves, &s.split) != 5)
+    return false;
+  s.variant = find_gemm_variant(s.mt, s.nt, s.kpw, s.waves);
+  if (s.variant < 0 || s.split < 1) return false;
+  if (N % (16 * s.nt) != 0) return false;
+  const int ks = (K + 127) / 128;
+  if ((ks + s.split * s.waves - 1) / (s.split * s.waves) > s.kpw) return false;
+  const int tiles = (N / (16 * s.nt)) * ((M + 16 * s.mt - 1) / (16 * s.mt));
+  if (s.split > 1 && tiles > kMaxSplitTiles) return false;
+  *out = s;
+  return true;
+}
+
+bool choose(int M, int N, int K, Schedule *s) {
+  {
+    std::lock_guard<std::mutex> lk(g_opt_mu);
+    if (g_schedule_override_set) return parse_schedule(g_schedule_override, M, N, K, s);
+  }
+  return pick_schedule(M, N, K, s);
+}
+
+mxfp4_status_t check_gemm_args(const void *A, const void *Bq, const void *Bs, const void *C, int64_t M, int64_t N,
+                               int64_t K) {
+  if (!A || !Bq || !Bs || !C) return MXFP4_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < 1) return MXFP4_ERR_INVALID_ARG;
+  if (!aligned(A, 16) || !aligned(Bq, 16) || !aligned(Bs, 16) || !aligned(C, 16)) return MXFP4_ERR_INVALID_ARG;
+  if (K % 64 != 0 || N % 32 != 0) return MXFP4_ERR_UNSUPPORTED;
+  if (M * K * 2 >= kMaxBytes || N * K / 2 >= kMaxBytes || M * N * 2 >= kMaxBytes ||
+      pad_to(N, 256) * pad_to(K / 32, 8) >= kMaxBytes)
+    return MXFP4_ERR_UNSUPPORTED;
+  return MXFP4_OK;
+}
+
+// Library-owned workspaces, one per (device, stream).
+struct WsEntry {
+  int device;
+  void *stream;
+  void *ptr;
+  size_t bytes;
+};
+std::mutex g_ws_mu;
+std::vector<WsEntry> g_ws;
+
+mxfp4_status_t get_workspace(size_t need, hipStream_t stream, void **out) {
+  *out = nullptr;
+  if (need == 0) return MXFP4_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MXFP4_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  for (auto &e : g_ws) {
+    if (e.device == dev && e.stream == (void *)stream) {
+      if (e.bytes >= need) {
+        *out = e.ptr;
+        return MXFP4_OK;
+      }
+      // grow: wait for work that may still use the old buffer
+      if (hipStreamSynchronize(stream) != hipSuccess) return MXFP4_ERR_HIP;
+      if (hipFree(e.ptr) != hipSuccess) return MXFP4_ERR_HIP;
+      e.ptr = nullptr;
+      e.bytes = 0;
+      if (hipMalloc(&e.ptr, need) != hipSuccess) return MXFP4_ERR_HIP;
+      if (hipMemsetAsync(e.ptr, 0, need, stream) != hipSuccess) return MXFP4_ERR_HIP;
+      e.bytes = need;
+      *out = e.ptr;
+      return MXFP4_OK;
+    }
+  }
+  WsEntry e{dev, (void *)stream, nullptr, 0};
+  if (hipMalloc(&e.ptr, need) != hipSuccess) return MXFP4_ERR_HIP;
+  if (hipMemsetAsync(e.ptr, 0, need, stream) != hipSuccess) {
+    (void)hipFree(e.ptr);
+    return MXFP4_ERR_HIP;
+  }
+  e.bytes = need;
+  g_ws.push_back(e);
+  *out = e.ptr;
+  return MXFP4_OK;
+}
+
+bool sw_quant() {
+  std::lock_guard<std::mutex> lk(g_opt_mu);
+  return g_quant_mode == 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mxfp4_packed_bytes(int64_t rows, int64_t K) { return rows > 0 && K > 0 ? (size_t)(rows * K / 2) : 0; }
+
+size_t mxfp4_raw_scale_bytes(int64_t rows, int64_t K) { return rows > 0 && K > 0 ? (size_t)(rows * (K / 32)) : 0; }
+
+size_t mxfp4_shuffled_scale_bytes(int64_t rows, int64_t K) {
+  return rows > 0 && K > 0 ? (size_t)(pad_to(rows, 256) * pad_to(K / 32, 8)) : 0;
+}
+
+size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1 || K % 64 != 0 || N % 32 != 0) return 0;
+  Schedule s;
+  if (!choose((int)M, (int)N, (int)K, &s)) return 0;
+  return gemm_workspace_bytes(s, (int)M, (int)N, (int)K);
+}
+
+const char *mxfp4_status_string(mxfp4_status_t st) {
+  switch (st) {
+    case MXFP4_OK: return "MXFP4_OK";
+    case MXFP4_ERR_INVALID_ARG: return "MXFP4_ERR_INVALID_ARG: null pointer, non-positive size or misaligned pointer";
+    case MXFP4_ERR_UNSUPPORTED: return "MXFP4_ERR_UNSUPPORTED: shape not handled (needs K % 64 == 0, N % 32 == 0)";
+    case MXFP4_ERR_WORKSPACE: return "MXFP4_ERR_WORKSPACE: workspace missing or too small";
+    case MXFP4_ERR_HIP: return "MXFP4_ERR_HIP: a HIP call or kernel launch failed";
+  }
+  return "MXFP4: unknown status";
+}
+
+const char *mxfp4_gemm_schedule_name(int64_t M, int64_t N, int64_t K) {
+  static thread_local char buf[96];
+  if (M < 1 || N < 1 || K < 1 || K % 64 != 0 || N % 32 != 0) return nullptr;
+  Schedule s;
+  if (!choose((int)M, (int)N, (int)K, &s)) return nullptr;
+  snprintf(buf, sizeof(buf), "mt%d_nt%d_kpw%d_w%d_split%d", s.mt, s.nt, s.kpw, s.waves, s.split);
+  return buf;
+}
+
+/* Testing and fallback knobs (declared in mxfp4.h). */
+mxfp4_status_t mxfp4_set_quant_mode(int mode) {
+  if (mode != 0 && mode != 1) return MXFP4_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_opt_mu);
+  g_quant_mode = mode;
+  return MXFP4_OK;
+}
+
+mxfp4_status_t mxfp4_set_schedule_override(const char *name) {
+  std::lock_guard<std::mutex> lk(g_opt_mu);
+  if (!name || !*name) {
+    g_schedule_override_set = false;
+    g_schedule_override.clear();
+    return MXFP4_OK;
+  }
+  int a, b, c, d, e;
+  if (sscanf(name, "mt%d_nt%d_kpw%d_w%d_split%d", &a, &b, &c, &d, &e) != 5 || find_gemm_variant(a, b, c, d) < 0 ||
+      e < 1)
+    return MXFP4_ERR_INVALID_ARG;
+  g_schedule_override = name;
+  g_schedule_override_set = true;
+  return MXFP4_OK;
+}
+
+mxfp4_status_t mxfp4_quantize(const void *x_bf16, int64_t rows, int64_t K, void *q, void *scales,
+                              int shuffled_scales, mxfp4_stream_t stream) {
+  if (!x_bf16 || !q || !scales) return MXFP4_ERR_INVALID_ARG;
+  if (rows < 1 || K < 32) return MXFP4_ERR_INVALID_ARG;
+  if (!aligned(x_bf16, 16) || !aligned(q, 16)) return MXFP4_ERR_INVALID_ARG;
+  if (K % 32 != 0) return MXFP4_ERR_UNSUPPORTED;
+  if (rows * K * 2 >= kMaxBytes || pad_to(rows, 256) * pad_to(K / 32, 8) >= kMaxBytes) return MXFP4_ERR_UNSUPPORTED;
+  hipError_t e = launch_quantize(x_bf16, rows, K, q, scales, shuffled_scales != 0, sw_quant(), (hipStream_t)stream);
+  return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+}
+
+mxfp4_status_t mxfp4_preshuffle_b(const void *bq, const void *bs_raw, int64_t N, int64_t K, void *bq_shuffled,
+                                  void *bs_shuffled, mxfp4_stream_t stream) {
+  if (!bq || !bs_raw || !bq_shuffled || !bs_shuffled) return MXFP4_ERR_INVALID_ARG;
+  if (N < 1 || K < 32) return MXFP4_ERR_INVALID_ARG;
+  if (!aligned(bq, 16) || !aligned(bq_shuffled, 16)) return MXFP4_ERR_INVALID_ARG;
+  if (N % 16 != 0 || K % 32 != 0) return MXFP4_ERR_UNSUPPORTED;
+  if (N * K / 2 >= kMaxBytes || pad_to(N, 256) * pad_to(K / 32, 8) >= kMaxBytes) return MXFP4_ERR_UNSUPPORTED;
+  hipError_t e = launch_preshuffle_b(bq, bs_raw, N, K, bq_shuffled, bs_shuffled, (hipStream_t)stream);
+  return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+}
+
+mxfp4_status_t mxfp4_gemm_ex(const void *A, const void *Bq_sh, const void *Bs_sh, void *C, int64_t M, int64_t N,
+                             int64_t K, void *workspace, size_t workspace_bytes, mxfp4_stream_t stream) {
+  mxfp4_status_t st = check_gemm_args(A, Bq_sh, Bs_sh, C, M, N, K);
+  if (st != MXFP4_OK) return st;
+  Schedule s;
+  if (!choose((int)M, (int)N, (int)K, &s)) return MXFP4_ERR_UNSUPPORTED;
+  const size_t need = gemm_workspace_bytes(s, (int)M, (int)N, (int)K);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return MXFP4_ERR_WORKSPACE;
+  GemmArgs a{A, Bq_sh, Bs_sh, C, workspace, (int)M, (int)N, (int)K};
+  return launch_gemm(s, a, sw_quant(), (hipStream_t)stream) == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+}
+
+mxfp4_status_t mxfp4_gemm(const void *A, const void *Bq_sh, const void *Bs_sh, void *C, int64_t M, int64_t N,
+                          int64_t K, mxfp4_stream_t stream) {
+  mxfp4_status_t st = check_gemm_args(A, Bq_sh, Bs_sh, C, M, N, K);
+  if (st != MXFP4_OK) return st;
+  Schedule s;
+  if (!choose((int)M, (int)N, (int)K, &s)) return MXFP4_ERR_UNSUPPORTED;
+  const size_t need = gemm_workspace_bytes(s, (int)M, (int)N, (int)K);
+  void *ws = nullptr;
+  st = get_workspace(need, (hipStream_t)stream, &ws);
+  if (st != MXFP4_OK) return st;
+  GemmArgs a{A, Bq_sh, Bs_sh, C, ws, (int)M, (int)N, (int)K};
+  return launch_gemm(s, a, sw_quant(), (hipStream_t)stream) == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+}
+
+mxfp4_status_t mxfp4_reserve(int64_t M, int64_t N, int64_t K, mxfp4_stream_t stream) {
+  if (M < 1 || N < 1 || K < 1) return MXFP4_ERR_INVALID_ARG;
+  if (K % 64 != 0 || N % 32 != 0) return MXFP4_ERR_UNSUPPORTED;
+  Schedule s;
+  if (!choose((int)M, (int)N, (int)K, &s)) return MXFP4_ERR_UNSUPPORTED;
+  void *ws = nullptr;
+  return get_workspace(gemm_workspace_bytes(s, (int)M, (int)N, (int)K), (hipStream_t)stream, &ws);
+}
+
+}  // extern "C"

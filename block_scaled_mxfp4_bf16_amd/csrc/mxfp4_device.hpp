@@ -1,0 +1,128 @@
+// Device helpers for the gfx950 MXFP4 kernels: group scale, e2m1 encoders,
+// bf16 rounding and the shuffled-scale address.
+//
+// Sources: submission 608632 (_hw_mxfp4_quant_op, steps 1-3), submission
+// 711914 (_mxfp4_quant_tile, _standalone_quant_kernel).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxfp4 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Scale byte of a group from the largest |x| given as bf16 magnitude bits
+// (15 bits, sign cleared).  The f32 pattern of amax is those bits << 16.
+// Adding 2^21 and masking the mantissa keeps the exponent unless the top two
+// mantissa bits are both set, where it moves up by one; the e8m0 byte is
+// that exponent minus 2, clamped to [0, 254] (submission 608632,
+// _hw_mxfp4_quant_op, step 1).
+__device__ __forceinline__ uint32_t scale_byte_from_amax(uint32_t amax_mag16) {
+  uint32_t r = ((amax_mag16 << 16) + 0x00200000u) & 0xFF800000u;
+  int e = (int)(r >> 23);
+  e -= 2;
+  e = e < 0 ? 0 : e;
+  e = e > 254 ? 254 : e;
+  return (uint32_t)e;
+}
+
+// Largest magnitude of 32 bf16 values held as 16 dwords (two per dword),
+// as 15-bit magnitude bits.  Integer order of the magnitude bits equals
+// value order for finite inputs.
+__device__ __forceinline__ uint32_t amax_mag16(const uint32_t (&w)[16]) {
+  u16x2 m = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t a = w[i] & 0x7FFF7FFFu;
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, a));
+  }
+  return m.x > m.y ? m.x : m.y;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Hardware encode: v_cvt_scalef32_pk_fp4_f32 converts two f32 values divided
+// by the power of two whose exponent field is the scale's, and writes the two
+// codes (first operand low nibble) into byte `sel` of the destination
+// (submission 608632, _hw_mxfp4_quant_op, step 3; submission 711914,
+// _mxfp4_quant_tile_hw).  The scale float is built with exponent field s.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_pair_hw(uint32_t old, uint32_t w, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, bf16_lo(w), bf16_hi(w), scale, SEL);
+}
+
+// Software encode of one element, written from the rounding rule itself:
+// v = |x| / 2^(s-127) is exact in f32 (bf16 input, power-of-two divisor;
+// results in the subnormal range are far below the first decision point).
+// The e2m1 grid has spacing 0.5 below 2, 1 in [2, 4) and 2 from 4 up, so
+// rounding v to that grid with rint (nearest, ties to even) gives the code
+// directly; 6 is the largest value.
+__device__ __forceinline__ uint32_t encode_sw(uint32_t xbits16, float inv_scale) {
+  float v = __uint_as_float((xbits16 & 0x7FFFu) << 16) * inv_scale;
+  v = fminf(v, 8.0f);
+  uint32_t code;
+  if (v < 2.0f) code = (uint32_t)__builtin_rintf(v * 2.0f);
+  else if (v < 4.0f) code = (uint32_t)__builtin_rintf(v) + 2u;
+  else code = min((uint32_t)__builtin_rintf(v * 0.5f) + 4u, 7u);
+  return code | ((xbits16 >> 12) & 0x8u);
+}
+
+// 2^(127 - s) as f32 (s in [0, 254]; s = 254 gives the subnormal 2^-127).
+__device__ __forceinline__ float inv_scale_f32(uint32_t s) {
+  return s < 254 ? __uint_as_float((254u - s) << 23) : __uint_as_float(0x00400000u);
+}
+
+// Quantize one 32-element group (16 dwords of bf16 pairs, element 2i in the
+// low half of w[i]) to 16 bytes of packed codes (q[0..3], element 2i in the
+// low nibble of byte i) and return the scale byte.
+template <bool SW>
+__device__ __forceinline__ uint32_t quant_group32(const uint32_t (&w)[16], uint32_t (&q)[4]) {
+  uint32_t s = scale_byte_from_amax(amax_mag16(w));
+  if constexpr (!SW) {
+    float sf = __uint_as_float(s << 23);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t d = 0;
+      d = cvt_pair_hw<0>(d, w[4 * j + 0], sf);
+      d = cvt_pair_hw<1>(d, w[4 * j + 1], sf);
+      d = cvt_pair_hw<2>(d, w[4 * j + 2], sf);
+      d = cvt_pair_hw<3>(d, w[4 * j + 3], sf);
+      q[j] = d;
+    }
+  } else {
+    float inv = inv_scale_f32(s);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t d = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        uint32_t x = w[4 * j + b];
+        uint32_t lo = encode_sw(x & 0xFFFFu, inv);
+        uint32_t hi = encode_sw(x >> 16, inv);
+        d |= (lo | (hi << 4)) << (8 * b);
+      }
+      q[j] = d;
+    }
+  }
+  return s;
+}
+
+// f32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Byte offset of (row, group) in a shuffled scale buffer whose rows of 32
+// hold gp = pad8(K/32) groups each (see mxfp4_shuffled_scale_bytes).
+__device__ __forceinline__ uint32_t shuffled_scale_offset(uint32_t row, uint32_t g, uint32_t gp) {
+  uint32_t in_block = ((row >> 4) & 1u) | (((g >> 2) & 1u) << 1) | ((row & 15u) << 2) | ((g & 3u) << 6);
+  return in_block + ((g >> 3) << 8) + (row >> 5) * 32u * gp;
+}
+
+}  // namespace mxfp4

@@ -1,0 +1,51 @@
+// Host-side declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mxfp4 {
+
+// A GEMM schedule: compile-time tile shape plus the runtime split count.
+//   mt    16-row M tiles per workgroup (the WG covers 16*mt rows)
+//   nt    16-column N subtiles per wave (all waves of a WG share them)
+//   kpw   most 128-wide K steps one wave handles
+//   waves waves per WG; they split the WG's K range and reduce through LDS
+//   split WGs that split K for one output tile; the last to finish adds the
+//         partial sums from the workspace and stores C
+struct Schedule {
+  int mt, nt, kpw, waves, split;
+  int variant;  // index into the kernel table
+};
+
+// Split-K workspace layout: a fixed prefix of ticket words (one per output
+// tile, zero between calls), then the f32 partial tiles.  The prefix has the
+// same size for every shape, so a workspace can serve shapes one after
+// another without the partials of one landing on the tickets of the next.
+constexpr size_t kTicketBytes = 65536;
+constexpr int kMaxSplitTiles = (int)(kTicketBytes / 4);
+
+struct GemmArgs {
+  const void *A;
+  const void *Bw;
+  const void *Bs;
+  void *C;
+  void *workspace;
+  int M, N, K;
+};
+
+// Kernel table queries (gemm_kernels.hip).
+int num_gemm_variants();
+void gemm_variant_shape(int v, int *mt, int *nt, int *kpw, int *waves);
+int find_gemm_variant(int mt, int nt, int kpw, int waves);
+
+size_t gemm_workspace_bytes(const Schedule &s, int M, int N, int K);
+hipError_t launch_gemm(const Schedule &s, const GemmArgs &a, bool sw_quant, hipStream_t stream);
+
+hipError_t launch_quantize(const void *x, int64_t rows, int64_t K, void *q, void *scales, bool shuffled, bool sw,
+                           hipStream_t stream);
+hipError_t launch_preshuffle_b(const void *bq, const void *bs_raw, int64_t N, int64_t K, void *bq_sh, void *bs_sh,
+                               hipStream_t stream);
+
+}  // namespace mxfp4

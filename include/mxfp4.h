@@ -1,0 +1,183 @@
+/*
+ * mxfp4.h -- C ABI of the MI355X (gfx950) MXFP4 GEMM library (libmxfp4.so).
+ *
+ *   C[M,N] (bf16) = Q(A[M,K] bf16) * B[N,K]^T
+ *
+ * A is quantized at call time to MXFP4: one e8m0 power-of-two scale per 32
+ * consecutive K elements, e2m1 elements; B is MXFP4 prepared once, offline,
+ * in the preshuffled layouts below.
+ *
+ * Sources (web pages, each a diff between two versions of a submission to
+ * the "amd-mxfp4-mm" leaderboard; cited by submission number):
+ *   submission 608632  (hardware FP4 convert; kernel v7; bypass launchers)
+ *   submission 610679  (constexpr kernels; split-K launcher + reduce)
+ *   submission 711914  (three-path dispatch; standalone quant kernel)
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers (hipMalloc'ed or equivalent) unless said
+ *     otherwise.  The caller owns every buffer; the library never frees or
+ *     retains them beyond the call.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *     Work is enqueued asynchronously; no entry point synchronizes the host.
+ *   - Arguments are checked on the host before anything is enqueued; a
+ *     failed check returns an error and enqueues nothing.  Device faults
+ *     surface at the caller's next synchronization, as usual in HIP.
+ *   - Pointers that the kernels read or write in 16-byte vectors (bf16 and
+ *     packed FP4 matrices, and C) must be 16-byte aligned.
+ *   - Inputs must be finite; NaN/Inf in A or B are outside the method.
+ */
+#ifndef MXFP4_H
+#define MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MXFP4_API __attribute__((visibility("default")))
+#else
+#define MXFP4_API
+#endif
+
+typedef void *mxfp4_stream_t; /* a hipStream_t */
+
+typedef enum {
+    MXFP4_OK = 0,
+    MXFP4_ERR_INVALID_ARG = 1, /* null pointer, size <= 0, misaligned pointer  */
+    MXFP4_ERR_UNSUPPORTED = 2, /* shape outside what the kernels handle         */
+    MXFP4_ERR_WORKSPACE = 3,   /* caller workspace too small                    */
+    MXFP4_ERR_HIP = 4          /* a HIP call or kernel launch failed            */
+} mxfp4_status_t;
+
+/* ------------------------------------------------------------------------ */
+/* Sizes (host only, pure).                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Packed e2m1 bytes of a [rows, K] matrix: rows * K / 2.  Element 2i of a
+ * row sits in the low nibble of byte i, element 2i+1 in the high nibble
+ * (submission 608632, _hw_mxfp4_quant_op, step 3). */
+MXFP4_API size_t mxfp4_packed_bytes(int64_t rows, int64_t K);
+
+/* Natural-layout scales: rows * (K / 32) bytes, row-major. */
+MXFP4_API size_t mxfp4_raw_scale_bytes(int64_t rows, int64_t K);
+
+/* Shuffled scales: pad256(rows) * pad8(K / 32) bytes, viewed as
+ * [pad256(rows) / 32, pad8(K / 32) * 32] (submission 608632, bypass
+ * launchers, the s0/s1 padding of the scale buffer).  Byte of (row, g):
+ *   row = 32*r0 + 16*r1 + r2,  g = 8*k0 + 4*k1 + k2,
+ *   r1 + 2*k1 + 4*r2 + 64*k2 + 256*k0 + r0 * 32 * pad8(K/32)
+ * (submission 608632, _shuffle_scales; submission 711914, the address
+ * arithmetic of _standalone_quant_kernel).  Padding bytes are 127 (2^0),
+ * the fill submission 711914 gives its scale buffer. */
+MXFP4_API size_t mxfp4_shuffled_scale_bytes(int64_t rows, int64_t K);
+
+/* Workspace bytes mxfp4_gemm_ex needs for this shape (split-K partial sums
+ * and per-tile tickets); 0 when the chosen schedule needs none. */
+MXFP4_API size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* ------------------------------------------------------------------------ */
+/* Quantize a bf16 matrix to MXFP4.                                           */
+/* Per 32-element group along K: amax = max |x| in f32; R = (bits(amax) +    */
+/* 0x200000) & 0xFF800000; scale byte s = clamp(exponent(R) - 2, 0, 254)     */
+/* (submission 608632, _hw_mxfp4_quant_op, steps 1-2).  Each element is      */
+/* x / 2^(s-127) rounded to the nearest e2m1 value, ties to even, saturated  */
+/* at 6, sign kept (submission 711914, _mxfp4_quant_tile).                   */
+/*                                                                           */
+/*   x_bf16   [rows, K] bf16, row-major, 16-byte aligned          (input)    */
+/*   q        [rows, K/2] bytes, 16-byte aligned                  (output)   */
+/*   scales   raw [rows, K/32] (shuffled_scales == 0), or the shuffled,      */
+/*            padded buffer of mxfp4_shuffled_scale_bytes bytes, padding      */
+/*            written as 127 (shuffled_scales != 0)                (output)   */
+/* Errors: INVALID_ARG (null, rows < 1, K < 32, misaligned x or q);          */
+/*         UNSUPPORTED (K % 32 != 0, sizes beyond 2^31 bytes).               */
+/* ------------------------------------------------------------------------ */
+MXFP4_API mxfp4_status_t mxfp4_quantize(const void *x_bf16, int64_t rows, int64_t K, void *q, void *scales,
+                              int shuffled_scales, mxfp4_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Rearrange quantized B into the layouts mxfp4_gemm reads.                  */
+/*   bq          [N, K/2] packed e2m1, natural layout, 16-byte aligned        */
+/*   bs_raw      [N, K/32] raw scales                                         */
+/*   bq_shuffled [N/16, (K/2)*16] bytes: 16-row x 16-byte tiles, each 256    */
+/*               contiguous bytes row-major, tiles of a 16-row group          */
+/*               consecutive along K, groups consecutive:                     */
+/*               out[g*(K/2)*16 + t*256 + n*16 + j] = bq[16g+n][16t+j]        */
+/*               (the layout whose inverse submissions 608632, kernel v7,     */
+/*               and 711914, _unshuffle_b_preshuffle, print)                  */
+/*   bs_shuffled mxfp4_shuffled_scale_bytes(N, K) bytes, as above             */
+/* Errors: INVALID_ARG (null, N < 1, K < 32, misaligned);                    */
+/*         UNSUPPORTED (N % 16 != 0, K % 32 != 0, sizes beyond 2^31 bytes). */
+/* ------------------------------------------------------------------------ */
+MXFP4_API mxfp4_status_t mxfp4_preshuffle_b(const void *bq, const void *bs_raw, int64_t N, int64_t K, void *bq_shuffled,
+                                  void *bs_shuffled, mxfp4_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* The fused GEMM: quantize A on the fly (as mxfp4_quantize), multiply by    */
+/* the preshuffled B with scaled FP4 matrix instructions, accumulate in f32, */
+/* round to bf16 (nearest even) and store C.  (submission 608632, kernel v7: */
+/* quant of the bf16 A tile inside the K loop, scaled e2m1 x e2m1 dot into   */
+/* an f32 accumulator, bf16 store; submission 610679, split-K kernel +       */
+/* reduce: here the reduction happens inside the same launch.)               */
+/*                                                                           */
+/*   A       [M, K] bf16 row-major, 16-byte aligned                (input)   */
+/*   Bq_sh   bq_shuffled of mxfp4_preshuffle_b, 16-byte aligned    (input)   */
+/*   Bs_sh   bs_shuffled of mxfp4_preshuffle_b, 16-byte aligned    (input)   */
+/*   C       [M, N] bf16 row-major, fully overwritten; must not alias the    */
+/*           inputs; 16-byte aligned                                (output) */
+/* mxfp4_gemm uses a library-owned workspace per (device, stream), created   */
+/* on the first call for a shape that needs more (that call allocates;       */
+/* later calls do not).  Results are deterministic: the split-K partial sums */
+/* are added in a fixed order.                                               */
+/* Errors: INVALID_ARG (null, M/N/K < 1, misaligned);                        */
+/*         UNSUPPORTED (K % 64 != 0 -- the harness's precondition, submission */
+/*         608632 input generator --, N % 32 != 0, sizes beyond 2^31 bytes); */
+/*         HIP (allocation or launch failure).                               */
+/* ------------------------------------------------------------------------ */
+MXFP4_API mxfp4_status_t mxfp4_gemm(const void *A, const void *Bq_sh, const void *Bs_sh, void *C, int64_t M, int64_t N,
+                          int64_t K, mxfp4_stream_t stream);
+
+/* As mxfp4_gemm with a caller-owned workspace of at least
+ * mxfp4_gemm_workspace_bytes(M, N, K) bytes, 256-byte aligned.  Its first
+ * 65536 bytes hold one ticket word per output tile and must be zero before
+ * the first use (zero-fill the whole buffer once); every call leaves them at
+ * zero again, so later calls -- also for other shapes -- need no clearing.
+ * The rest holds f32 partial sums.  Calls that share a workspace must not
+ * overlap in time.
+ * Errors: as mxfp4_gemm, plus WORKSPACE (too small or null when needed). */
+MXFP4_API mxfp4_status_t mxfp4_gemm_ex(const void *A, const void *Bq_sh, const void *Bs_sh, void *C, int64_t M, int64_t N,
+                             int64_t K, void *workspace, size_t workspace_bytes, mxfp4_stream_t stream);
+
+/* Create the library-owned workspace for (M, N, K) on `stream` ahead of time
+ * (so that no later mxfp4_gemm call allocates, e.g. under graph capture). */
+MXFP4_API mxfp4_status_t mxfp4_reserve(int64_t M, int64_t N, int64_t K, mxfp4_stream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+MXFP4_API const char *mxfp4_status_string(mxfp4_status_t status);
+
+/* Name of the kernel schedule mxfp4_gemm picks for a shape (thread-local
+ * storage, valid until the next call on the thread), e.g.
+ * "mt1_nt2_kpw4_w4_split2"; NULL if the shape is unsupported. */
+MXFP4_API const char *mxfp4_gemm_schedule_name(int64_t M, int64_t N, int64_t K);
+
+/* Process-wide choice of the e2m1 encoder used by mxfp4_quantize and the
+ * fused GEMM: 0 = the hardware convert (default), 1 = a software encoder
+ * (the pages keep such a fallback next to the hardware path: submission
+ * 608632, the warmup self-check and USE_HW_QUANT switch).  Both produce
+ * identical bytes.  Not to be changed while calls are in flight.
+ * Errors: INVALID_ARG for any other mode. */
+MXFP4_API mxfp4_status_t mxfp4_set_quant_mode(int mode);
+
+/* Process-wide schedule override for mxfp4_gemm, by the name format of
+ * mxfp4_gemm_schedule_name (for tuning sweeps); NULL or "" restores the
+ * built-in choice.  A call whose shape the override cannot serve returns
+ * UNSUPPORTED.  Errors: INVALID_ARG for a name no compiled kernel matches. */
+MXFP4_API mxfp4_status_t mxfp4_set_schedule_override(const char *name);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H */

@@ -1,0 +1,125 @@
+"""The C-ABI library loads on a machine without a GPU, exports every entry
+point include/mxfp4.h declares, and rejects bad arguments on the host before
+any HIP call (so no GPU is needed for these checks)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_mxfp4_bf16_amd as mx
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "mxfp4.h")
+
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declarations_match_binding():
+    assert declared_functions() == sorted(mx.exported_symbols())
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(mx.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_library_exports_nothing_else():
+    out = os.popen("nm -D --defined-only %s" % mx.LIB_PATH).read()
+    names = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    ours = {n for n in names if n.startswith("mxfp4")}
+    assert ours == set(declared_functions())
+
+
+def test_size_helpers():
+    assert mx.mxfp4_packed_bytes(16, 1536) == 16 * 768
+    assert mx.mxfp4_raw_scale_bytes(16, 1536) == 16 * 48
+    assert mx.mxfp4_shuffled_scale_bytes(2112, 7168) == 2304 * 224
+    assert mx.mxfp4_shuffled_scale_bytes(3072, 1536) == 3072 * 48
+    assert mx.mxfp4_shuffled_scale_bytes(16, 96) == 256 * 8
+    assert mx.mxfp4_packed_bytes(0, 64) == 0
+
+
+def test_status_strings():
+    L = mx.lib()
+    for code in range(5):
+        assert L.mxfp4_status_string(code).startswith(b"MXFP4")
+
+
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced (checks fail first)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, FAKE, FAKE, FAKE, 16, 64, 128), INVALID),           # null A
+    ((FAKE, FAKE, FAKE, 0, 16, 64, 128), INVALID),           # null C
+    ((FAKE, FAKE, FAKE, FAKE, 0, 64, 128), INVALID),         # M = 0
+    ((FAKE, FAKE, FAKE, FAKE, 16, -32, 128), INVALID),       # N < 0
+    ((FAKE + 8, FAKE, FAKE, FAKE, 16, 64, 128), INVALID),    # misaligned A
+    ((FAKE, FAKE, FAKE, FAKE, 16, 64, 96), UNSUPPORTED),     # K % 64 != 0
+    ((FAKE, FAKE, FAKE, FAKE, 16, 48, 128), UNSUPPORTED),    # N % 32 != 0
+    ((FAKE, FAKE, FAKE, FAKE, 1 << 16, 64, 1 << 15), UNSUPPORTED),  # A beyond 2^31 bytes
+])
+def test_gemm_rejects_bad_arguments(args, code):
+    L = mx.lib()
+    assert L.mxfp4_gemm(*args, None) == code
+    assert L.mxfp4_gemm_ex(*args, None, 0, None) == code
+
+
+def test_gemm_ex_rejects_small_workspace():
+    L = mx.lib()
+    M, N, K = 8, 2112, 7168
+    need = mx.mxfp4_gemm_workspace_bytes(M, N, K)
+    assert need > 0  # long K at small M splits K over workgroups
+    assert L.mxfp4_gemm_ex(FAKE, FAKE, FAKE, FAKE, M, N, K, None, 0, None) == WORKSPACE
+    assert L.mxfp4_gemm_ex(FAKE, FAKE, FAKE, FAKE, M, N, K, FAKE, need - 1, None) == WORKSPACE
+    assert L.mxfp4_gemm_ex(FAKE, FAKE, FAKE, FAKE, M, N, K, FAKE + 16, need, None) == WORKSPACE
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 16, 64, FAKE, FAKE, 0), INVALID),
+    ((FAKE, 0, 64, FAKE, FAKE, 0), INVALID),
+    ((FAKE, 16, 16, FAKE, FAKE, 0), INVALID),
+    ((FAKE, 16, 48, FAKE, FAKE, 0), UNSUPPORTED),
+    ((FAKE + 4, 16, 64, FAKE, FAKE, 0), INVALID),
+])
+def test_quantize_rejects_bad_arguments(args, code):
+    assert mx.lib().mxfp4_quantize(*args, None) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((FAKE, FAKE, 24, 64, FAKE, FAKE), UNSUPPORTED),
+    ((FAKE, FAKE, 32, 48, FAKE, FAKE), UNSUPPORTED),
+    ((FAKE, 0, 32, 64, FAKE, FAKE), INVALID),
+])
+def test_preshuffle_rejects_bad_arguments(args, code):
+    assert mx.lib().mxfp4_preshuffle_b(*args, None) == code
+
+
+def test_schedule_names_and_override():
+    name = mx.mxfp4_gemm_schedule_name(16, 3072, 1536)
+    assert re.fullmatch(r"mt\d+_nt\d+_kpw\d+_w\d+_split\d+", name)
+    assert mx.mxfp4_gemm_schedule_name(16, 3072, 96) is None
+    with pytest.raises(RuntimeError):
+        mx.mxfp4_set_schedule_override("mt9_nt9_kpw9_w9_split1")
+    mx.mxfp4_set_schedule_override("mt1_nt2_kpw4_w4_split3")
+    try:
+        assert mx.mxfp4_gemm_schedule_name(16, 3072, 1536) == "mt1_nt2_kpw4_w4_split3"
+        # an override that cannot cover K: the shape is unsupported under it
+        assert mx.mxfp4_gemm_schedule_name(16, 3072, 7168 * 4) is None
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+    assert mx.mxfp4_gemm_schedule_name(16, 3072, 1536) == name
+
+
+def test_quant_mode_knob():
+    with pytest.raises(RuntimeError):
+        mx.mxfp4_set_quant_mode(2)
+    mx.mxfp4_set_quant_mode(1)
+    mx.mxfp4_set_quant_mode(0)

@@ -1,0 +1,185 @@
+"""GPU parity of the fused GEMM against the oracle, element by element:
+|C - C_ref| <= 1e-2 * |C_ref| + 1e-2 with C_ref the oracle's fp64 result on
+the same seeded inputs; B is given to the GPU as the oracle prepared it."""
+import numpy as np
+import pytest
+
+import block_scaled_mxfp4_bf16_amd as mx
+import oracle
+import synthetic as syn
+from tests.gpu_util import (assert_close, bf16_dev_to_bits, bits_to_f64, prepare_b, to_dev_u16_as_bf16,
+                            to_dev_u8, torch_cuda)
+
+pytestmark = pytest.mark.gpu
+
+
+class Case:
+    def __init__(self, torch, a_bits, b_bits):
+        self.torch = torch
+        self.M, self.K = a_bits.shape
+        self.N = b_bits.shape[0]
+        self.a_bits = a_bits
+        self.qb, self.sb, bw, bs = prepare_b(b_bits)
+        self.A = to_dev_u16_as_bf16(torch, a_bits)
+        self.Bw = to_dev_u8(torch, bw)
+        self.Bs = to_dev_u8(torch, bs)
+
+    def run(self):
+        C = mx.gemm(self.A, self.Bw, self.Bs, self.N)
+        self.torch.cuda.synchronize()
+        return bf16_dev_to_bits(C)
+
+    def ref(self):
+        qa, sa = oracle.quantize(self.a_bits)
+        return oracle.gemm_f64(qa, sa, self.qb, self.sb)
+
+    def ref_sampled(self, ms, ns):
+        qa, sa = oracle.quantize(self.a_bits)
+        return oracle.gemm_f64_sampled(qa, sa, self.qb, self.sb, ms, ns)
+
+
+def make(torch, M, N, K, seed):
+    return Case(torch, syn.normal_bf16(seed, syn.STREAM_A, (M, K)), syn.normal_bf16(seed, syn.STREAM_B, (N, K)))
+
+
+SMALL = [(1, 32, 64), (5, 64, 192), (16, 96, 256), (17, 160, 320), (33, 64, 512), (64, 128, 1024),
+         (100, 96, 384), (8, 2112, 448), (3, 32, 1088), (48, 64, 128), (130, 224, 2112)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_small_shapes_match_oracle(M, N, K):
+    torch = torch_cuda()
+    c = make(torch, M, N, K, seed=M * 7 + N + K)
+    assert_close(c.run(), c.ref(), "gemm %dx%dx%d" % (M, N, K))
+
+
+def test_one_hot_b_reproduces_fused_quantization_exactly():
+    """With B[n][k] = 1 at k = n, C[:, n] is the dequantized A column n: the
+    fused in-register quantization must equal the oracle's bit for bit
+    (the values are e2m1 times powers of two, exact in bf16)."""
+    torch = torch_cuda()
+    M, N, K = 24, 256, 256
+    a = syn.normal_bf16(17, syn.STREAM_A, (M, K))
+    a[3, 32:64] = 0  # a zero group
+    a[5, 0:32] = 0x8000
+    b = np.zeros((N, K), dtype=np.uint16)
+    b[np.arange(N), np.arange(N)] = 0x3F80
+    for mode in (0, 1):
+        mx.mxfp4_set_quant_mode(mode)
+        try:
+            got = Case(torch, a, b).run()
+        finally:
+            mx.mxfp4_set_quant_mode(0)
+        qa, sa = oracle.quantize(a)
+        want = oracle.bf16_from_f64(oracle.dequantize(qa, sa)[:, :N])
+        # -0.0 and +0.0 products sum to +0.0 in the matrix unit; compare values
+        assert np.array_equal(bits_to_f64(got), bits_to_f64(want)), "mode %d" % mode
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_config_full_match(name):
+    torch = torch_cuda()
+    w = syn.CONFIGS[name]
+    c = Case(torch, w.a_bits(), w.b_bits())
+    assert_close(c.run(), c.ref(), name)
+
+
+def test_config_c5_sampled():
+    """M=256, N=7168, K=7168: every output tile sampled, checked one by one."""
+    torch = torch_cuda()
+    w = syn.CONFIGS["c5"]
+    c = Case(torch, w.a_bits(), w.b_bits())
+    got = c.run()
+    rng = np.random.default_rng(5)
+    ms = np.concatenate([np.arange(0, 256, 16) + rng.integers(0, 16, 16)] * 4 + [rng.integers(0, 256, 1500)])
+    ns = np.concatenate([rng.integers(0, 7168, 64), rng.integers(0, 7168, 1500)])
+    ref = c.ref_sampled(ms, ns)
+    assert_close(got[ms, ns], ref, "c5 sampled")
+
+
+@pytest.mark.parametrize("name", list(syn.EXTRA_SHAPES))
+def test_leaderboard_shapes(name):
+    torch = torch_cuda()
+    w = syn.EXTRA_SHAPES[name]
+    c = Case(torch, w.a_bits(), w.b_bits())
+    got = c.run()
+    if w.M * w.N * w.K <= 3e8:
+        assert_close(got, c.ref(), name)
+    else:
+        rng = np.random.default_rng(1)
+        ms, ns = rng.integers(0, w.M, 3000), rng.integers(0, w.N, 3000)
+        assert_close(got[ms, ns], c.ref_sampled(ms, ns), name)
+
+
+SCHEDULES = ["mt1_nt2_kpw1_w4_split1", "mt1_nt2_kpw2_w4_split3", "mt1_nt2_kpw4_w4_split2",
+             "mt1_nt2_kpw8_w4_split1", "mt2_nt2_kpw1_w4_split4", "mt2_nt2_kpw2_w4_split1",
+             "mt4_nt2_kpw1_w4_split5", "mt4_nt2_kpw4_w4_split1", "mt4_nt2_kpw8_w4_split2"]
+
+
+@pytest.mark.parametrize("sched", SCHEDULES)
+def test_every_schedule_matches_oracle_and_is_deterministic(sched):
+    torch = torch_cuda()
+    c = make(torch, 40, 256, 2048 + 64, seed=3)
+    mx.mxfp4_set_schedule_override(sched)
+    try:
+        if mx.mxfp4_gemm_schedule_name(c.M, c.N, c.K) is None:
+            pytest.skip("schedule cannot cover this K")
+        first = c.run()
+        second = c.run()
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+    assert np.array_equal(first, second)
+    assert_close(first, c.ref(), sched)
+
+
+def test_hw_and_sw_encoders_give_identical_c():
+    torch = torch_cuda()
+    w = syn.CONFIGS["c4"]
+    c = Case(torch, w.a_bits(), w.b_bits())
+    hw = c.run()
+    mx.mxfp4_set_quant_mode(1)
+    try:
+        sw = c.run()
+    finally:
+        mx.mxfp4_set_quant_mode(0)
+    assert np.array_equal(hw, sw)
+
+
+def test_gemm_ex_with_caller_workspace():
+    torch = torch_cuda()
+    w = syn.CONFIGS["c3"]
+    c = Case(torch, w.a_bits(), w.b_bits())
+    need = mx.mxfp4_gemm_workspace_bytes(c.M, c.N, c.K)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        C = torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")
+        mx.mxfp4_gemm_ex(c.A, c.Bw, c.Bs, C, c.M, c.N, c.K, ws, need)
+        torch.cuda.synchronize()
+        outs.append(bf16_dev_to_bits(C))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+    assert np.array_equal(outs[0], c.run())
+    # the tickets are left at zero for the next call
+    assert int(ws[:65536].count_nonzero()) == 0
+
+
+def test_reserve_then_repeated_calls_are_identical():
+    torch = torch_cuda()
+    c = make(torch, 16, 3072, 1536, seed=1)
+    mx.mxfp4_reserve(c.M, c.N, c.K)
+    runs = [c.run() for _ in range(5)]
+    for r in runs[1:]:
+        assert np.array_equal(r, runs[0])
+
+
+def test_workspace_reused_across_shapes_with_more_tiles():
+    """A split-K shape with few tiles and a large partial region, then one
+    with more tiles on the same stream: the second one's tickets must not
+    land on the first one's partial sums."""
+    torch = torch_cuda()
+    first = make(torch, 130, 224, 2112, seed=21)   # 21 tiles, 5 splits of 16x64-row tiles
+    second = make(torch, 16, 3072, 1536, seed=22)  # 96 tiles, 3 splits
+    assert_close(first.run(), first.ref(), "first shape")
+    assert_close(second.run(), second.ref(), "second shape")
+    assert_close(first.run(), first.ref(), "first shape again")
