@@ -29,6 +29,48 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 matrix peak, TFLOP/s
 HEADLINE = "c2"
+KERNEL_SOURCES = ["block_scaled_mxfp4_bf16_amd/csrc/gemm_kernels.hip", "block_scaled_mxfp4_bf16_amd/csrc/mxfp4_device.hpp",
+                  "block_scaled_mxfp4_bf16_amd/csrc/mxfp4_api.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_M32_N4096_K512.json")
+CALIBRATION_BYTES = 256 << 20
+
+
+def calibration_copy(torch):
+    """A plain device copy of known size whose source is cold: 256 MiB
+    written, then 1 GiB written to push it out of L2 and the MALL, then
+    copied.  Counter runs scale HBM counters by what they read for it."""
+    src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    evict = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    evict.fill_(2)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, evict, dst
+    torch.cuda.empty_cache()
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the kernel as it is now; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
 
 
 def alg_bytes(M, N, K):
@@ -126,7 +168,61 @@ def cpu_baseline(w, budget_s=12.0):
             "sample": "%d whole calls of %s (quantize A + fp64 GEMM + bf16 rounding), %.1f s" % (n, w.name, el)}
 
 
+def _pmc_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir, command):
+    """Turn two rocprofv3 --pmc runs of the headline bench (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch) into HBM bytes per GEMM launch.  The scale
+    of each counter is calibrated on the plain copy kernels of the same runs
+    (the clones of B, of known size, made while preparing the buffer sets)."""
+    import synthetic as syn
+    w = syn.CONFIGS[HEADLINE]
+    bw_bytes = w.N * w.K // 2
+
+    def per_kernel(rows, counter):
+        gemm, copy = [], []
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"]) * 1024.0
+            name = r["Kernel_Name"]
+            if "gemm_kernel" in name:
+                gemm.append(v)
+            elif "copyBuffer" in name:
+                copy.append((int(r["Grid_Size"]), v))
+        # the calibration copy is the largest copy of the run
+        big = max(g for g, _ in copy)
+        return gemm, [v for g, v in copy if g == big]
+
+    fg, fc = per_kernel(_pmc_rows(fetch_dir), "FETCH_SIZE")
+    wg, wc = per_kernel(_pmc_rows(write_dir), "WRITE_SIZE")
+    med = lambda v: sorted(v)[len(v) // 2]
+    f_scale = med(fc) / CALIBRATION_BYTES  # counter bytes per byte copied
+    w_scale = med(wc) / CALIBRATION_BYTES
+    fetch = med(fg) / f_scale
+    write = med(wg) / w_scale
+    out = {"workload": w.name, "kernel_source_hash": kernel_source_hash(), "command": command,
+           "gemm_dispatches": [len(fg), len(wg)], "fetch_bytes_per_launch": round(fetch),
+           "write_bytes_per_launch": round(write), "hbm_bytes_per_launch": round(fetch + write),
+           "algorithmic_bytes": alg_bytes(w.M, w.N, w.K), "copy_calibration": {"fetch": f_scale, "write": w_scale}}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
+        summarize_pmc(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+        return
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
@@ -134,6 +230,8 @@ def main():
     ap.add_argument("--configs", default="c1,c2,c3,c4,c5", help="configurations measured under per_config")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="also time with one buffer set (caches warm)")
+    ap.add_argument("--pmc-calibration", action="store_true",
+                    help="first run a cold 256 MiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -148,6 +246,8 @@ def main():
     import synthetic as syn
 
     torch.cuda.set_device(0)
+    if args.pmc_calibration:
+        calibration_copy(torch)
     names = [c for c in args.configs.split(",") if c]
     if HEADLINE not in names:
         names.insert(0, HEADLINE)
@@ -164,6 +264,7 @@ def main():
 
     hw = syn.CONFIGS[HEADLINE]
     h = per[hw.name]
+    print("[bench] kernel source hash %s" % kernel_source_hash(), file=sys.stderr, flush=True)
     line = {
         "metric": "us/call and TFLOPS per (M,N,K); % of HBM or MXFP4-MFMA roofline",
         "value": h["tflops"],
@@ -186,7 +287,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(h["hbm_frac"], 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
         },
         "per_config": per,
     }

@@ -13,7 +13,8 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmxfp4.so")
+# MXFP4_LIB may point at another build of the same library (e.g. a debug build).
+LIB_PATH = os.environ.get("MXFP4_LIB") or os.path.join(_PKG, "libmxfp4.so")
 
 MXFP4_OK = 0
 

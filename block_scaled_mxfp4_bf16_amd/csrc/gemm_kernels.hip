@@ -4,11 +4,7 @@
 // operands e2m1 (format code 4), multiplies a 16x128 block of A by a 128x16
 // block of B^T, each 32-wide K chunk carrying its own e8m0 scale, into a
 // 16x16 f32 accumulator.  Lane l supplies row/column l%16 and K chunk l/16:
-// 32 e2m1 codes (16 bytes) and that chunk's scale byte.  A 32-wide K chunk is
-// exactly one scale group, so the quantization of A is lane-local: each lane
-// loads its 32 bf16 values (64 bytes), takes their amax, derives the scale
-// byte and converts with v_cvt_scalef32_pk_fp4_f32 (submission 608632,
-// kernel v7 and _hw_mxfp4_quant_op, which do the same per BLOCK_K tile).
+// 32 e2m1 codes (16 bytes) and that chunk's scale byte.
 //
 // B comes preshuffled (16-row x 16-byte tiles, 256 contiguous bytes each),
 // so the B operand of one instruction is 1 KiB contiguous and lane l loads
@@ -17,239 +13,708 @@
 // {l/16, l/16+4}: one dword per lane serves two 16-column subtiles and two
 // K steps (submission 711914, the vectorized scale loads of its kernels).
 //
-// Work split: a workgroup owns an output tile of 16*MT rows x 16*NT
-// columns; its WAVES waves take disjoint runs of 128-wide K steps (at most
-// KPW each) and add their accumulators through LDS in wave order.  When one
-// tile's K range is split over `split` workgroups (submission 610679, split-K
-// kernel), each writes its f32 partial tile to the workspace, then takes a
-// ticket; the workgroup that takes the last ticket adds the partials in
-// split order, stores bf16 C and resets the ticket.  The sum order is fixed,
-// so results are deterministic, and there is no second launch.
+// A is quantized inside the kernel (submission 608632, kernel v7, does the
+// same per BLOCK_K tile with the hardware convert) and staged through LDS,
+// once per workgroup, in the operand layout:
+//   - one load instruction covers 16 rows x one 32-element group: four
+//     consecutive lanes read one group's 64 contiguous bytes, so the access
+//     is coalesced (the operand layout read straight from memory would give
+//     every lane its own 64-byte run);
+//   - the four lanes of a group combine their amax with two DPP steps, then
+//     each converts its 8 elements with v_cvt_scalef32_pk_fp4_bf16 into one
+//     dword of codes;
+//   - lane t writes its dword at dword t of a 1 KiB block and the scale at
+//     byte t/4 + 16*kc; a block is exactly one matrix operand (operand lane L
+//     reads 16 bytes at 16*L), and both sides are free of bank conflicts.
+//
+// Work split: a workgroup owns an output tile of 16*MT rows x 16*NT*WN
+// columns and a run of K steps.  Its waves form a WN x WK grid: WN waves
+// share the staged A and take NT subtiles each; WK waves split the run
+// (KPW steps each) and add their accumulators through LDS in wave order.
+// When one tile's K range is split over `split` workgroups (submission
+// 610679, split-K kernel), each writes its f32 partial tile to the workspace
+// and takes a ticket; the workgroup that draws the last ticket adds the
+// partials in split order, stores bf16 C and resets the ticket.  The sum
+// order is fixed, so results are deterministic, and there is no second
+// launch (the pages reduce split-K partials with a second kernel).
 #include "mxfp4_device.hpp"
 #include "mxfp4_internal.hpp"
 
 namespace mxfp4 {
 
-template <int MT, int NT, int KPW, int WAVES, bool SW>
-__global__ __launch_bounds__(64 * WAVES) void gemm_fused_kernel(const uint16_t *__restrict__ A,
-                                                                const uint8_t *__restrict__ Bw,
-                                                                const uint8_t *__restrict__ Bs,
-                                                                uint16_t *__restrict__ C,
-                                                                float *__restrict__ partials,
-                                                                uint32_t *__restrict__ tickets, int M, int N,
-                                                                int K, int split, int n_tiles) {
-  constexpr int E = MT * NT * 256;  // outputs of one tile
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Word 3 of a gfx9 buffer resource for raw (untyped) dword access.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// DPP lane patterns within groups of four lanes.
+constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadSwap1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadSwap2, 0xF, 0xF, false));
+  return v;
+}
+
+// Quantize 8 consecutive elements of a 32-element group (4 dwords of bf16
+// pairs) whose other 24 elements sit in the three neighbouring lanes of the
+// same quad: returns the lane's dword of codes and writes the scale byte.
+__device__ __forceinline__ uint32_t quant_quarter(const u32x4 &w, int sw_quant, uint32_t *scale) {
+  u16x2 m = __builtin_bit_cast(u16x2, w.x & 0x7FFF7FFFu);
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.y & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.z & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.w & 0x7FFF7FFFu));
+  const uint32_t amax = quad_max(m.x > m.y ? m.x : m.y);
+  const uint32_t s = scale_byte_from_amax(amax);
+  *scale = s;
+  uint32_t d = 0;
+  if (!sw_quant) {
+    const float sf = __uint_as_float(s << 23);
+    d = cvt_pair_hw<0>(d, w.x, sf);
+    d = cvt_pair_hw<1>(d, w.y, sf);
+    d = cvt_pair_hw<2>(d, w.z, sf);
+    d = cvt_pair_hw<3>(d, w.w, sf);
+  } else {
+    const float inv = inv_scale_f32(s);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      d |= (encode_sw(ww[b] & 0xFFFFu, inv) | (encode_sw(ww[b] >> 16, inv) << 4)) << (8 * b);
+  }
+  return d;
+}
+
+template <int MT, int NT, int WN, int WK, int KPW, bool PREQ>
+__global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__restrict__ A,
+                                                           const uint8_t *__restrict__ Aop,
+                                                           const uint8_t *__restrict__ Bw,
+                                                           const uint8_t *__restrict__ Bs, uint16_t *__restrict__ C,
+                                                           float *__restrict__ partials,
+                                                           uint32_t *__restrict__ tickets, int M, int N, int K,
+                                                           int split, int n_tiles, int sw_quant) {
+  constexpr int WAVES = WN * WK;
   constexpr int NTH = 64 * WAVES;
-  __shared__ float red[WAVES][MT * NT * 4][64];
+  constexpr int KW = WK * KPW;                      // K steps one workgroup covers at most
+  constexpr int UNITS = KW * MT * 4;                // staged A blocks: 16 rows x 32 elements each
+  constexpr int UPW = (UNITS + WAVES - 1) / WAVES;  // per wave
+  constexpr int TN = NT * WN;                       // 16-column subtiles per workgroup
+  constexpr int E = MT * TN * 256;                  // outputs per tile
+  constexpr int NP = (NT + 1) / 2;                  // scale dwords per step and wave
+  constexpr int A_BYTES = PREQ ? 0 : KW * MT * 1024;  // codes
+  constexpr int S_BYTES = PREQ ? 0 : KW * MT * 64;    // scales
+  constexpr int RED_BYTES = WK > 1 ? WAVES * MT * NT * 1024 : 0;
+  constexpr int LDS_BYTES0 = (A_BYTES + S_BYTES) > RED_BYTES ? (A_BYTES + S_BYTES) : RED_BYTES;
+  constexpr int LDS_BYTES = LDS_BYTES0 > 16 ? LDS_BYTES0 : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   __shared__ uint32_t s_last;
+  uint32_t *a_lds = (uint32_t *)lds;
+  uint8_t *s_lds = lds + A_BYTES;
+  float *red = (float *)lds;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave % WN;
+  const int wk = wave / WN;
   const int bid = blockIdx.x;
   const int n_tile = bid % n_tiles;
   const int rest = bid / n_tiles;
   const int sk = rest % split;
   const int m_tile = rest / split;
   const int m0 = m_tile * 16 * MT;
-  const int g0 = n_tile * NT;  // first 16-row group of B (16-column subtile of C)
+  const int gw = n_tile * TN + wn * NT;  // this wave's first 16-row group of B
 
-  const int KS = (K + 127) >> 7;  // 128-wide K steps
-  const int W = split * WAVES;
-  const int wk = sk * WAVES + wave;
-  const int ks_begin = (int)(((int64_t)wk * KS) / W);
-  const int ks_end = (int)(((int64_t)(wk + 1) * KS) / W);
-
-  const int r16 = lane & 15;
-  const int kc = lane >> 4;
-  const size_t b_group_stride = (size_t)K * 8;  // (K/2) * 16 bytes per 16-row group
+  const int KS = (K + 127) >> 7;
+  const int S0 = (int)((uint32_t)(sk * KS) / (uint32_t)split);
+  const int S1 = (int)((uint32_t)((sk + 1) * KS) / (uint32_t)split);
   const int gp = ((K >> 5) + 7) & ~7;
-  const size_t s_block_stride = (size_t)gp * 32;  // bytes per 32-row block of scales
 
-  const uint16_t *arow[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    int r = m0 + 16 * mt + r16;
-    r = r < M ? r : M - 1;
-    arow[mt] = A + (size_t)r * K;
-  }
+  // Buffer descriptors carry the operands' byte sizes: a load whose offset
+  // is out of range returns zeros.  That is how rows past M, K chunks past K
+  // and steps past the run are handled, without branches: zero codes with a
+  // zero scale contribute nothing.
+  const int a_bytes = M * K * 2;
+  const int b_bytes = (N >> 4) * K * 8;
+  const int s_bytes = ((N + 255) >> 8) * 8 * gp * 32;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, a_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Bw, 0, b_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Bs, 0, s_bytes, kRsrcWord3);
 
-  // Phase 1: issue every load of this wave's K run.  Steps past the run are
-  // clamped to a valid step (their loads hit cache; their products are
-  // skipped); lanes past K in a half step (K % 128 == 64) load nothing.
-  uint32_t aw[KPW][MT][16];
-  uint4 bv[KPW][NT];
-  uint32_t sw[KPW][NT];
+  // Phase 1: issue the loads.  A first: it is small and mostly L2-resident,
+  // and since the load counter retires in issue order, quantizing it can
+  // then start while B (from HBM, the long pole) is still in flight.
+  const int kc = lane >> 4;
+  u32x4 aw[PREQ ? 1 : UPW];
+  u32x4 ap[PREQ ? KPW : 1][PREQ ? MT : 1];
+  uint32_t asb[PREQ ? KPW : 1][PREQ ? MT : 1];
+  if constexpr (!PREQ) {
 #pragma unroll
-  for (int i = 0; i < KPW; ++i) {
-    int ks = ks_begin + i;
-    ks = ks < KS ? ks : KS - 1;
-    const int kel = ks * 128 + kc * 32;
-    const bool valid = kel < K;
+    for (int u = 0; u < UPW; ++u) {
+      const int unit = wave + u * WAVES;  // (step, m tile, chunk) with the chunk fastest
+      const int st = unit / (MT * 4);
+      const int mt = (unit >> 2) % MT;
+      const int ch = unit & 3;
+      const int ks = S0 + st;
+      const int row = m0 + 16 * mt + (lane >> 2);
+      const int kel = ks * 128 + ch * 32 + (lane & 3) * 8;
+      const bool ok = (unit < UNITS) && (ks < S1) && (row < M) && (ks * 128 + ch * 32 < K);
+      aw[u] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ok ? (row * K + kel) * 2 : a_bytes, 0, 0);
+    }
+  } else {
+    // pre-quantized A in operand blocks: per (m tile, step) 1 KiB of codes,
+    // lane L's 16 bytes at 16*L, then 64 scale bytes
+    const int op_bytes = ((M + 15) >> 4) * KS * 1088;
+    const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Aop, 0, op_bytes, kRsrcWord3);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint4 *src = (const uint4 *)(arow[mt] + kel);
+    for (int i = 0; i < KPW; ++i) {
+      const int ks = S0 + wk * KPW + i;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint4 v = valid ? src[j] : make_uint4(0, 0, 0, 0);
-        aw[i][mt][4 * j + 0] = v.x;
-        aw[i][mt][4 * j + 1] = v.y;
-        aw[i][mt][4 * j + 2] = v.z;
-        aw[i][mt][4 * j + 3] = v.w;
+      for (int mt = 0; mt < MT; ++mt) {
+        const int mtile = m_tile * MT + mt;
+        const bool ok = (ks < S1) && (mtile * 16 < M);
+        const int blk = (mtile * KS + ks) * 1088;
+        ap[i][mt] = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, ok ? blk + lane * 16 : op_bytes, 0, 0);
+        asb[i][mt] = __builtin_amdgcn_raw_buffer_load_b8(q_rsrc, ok ? blk + 1024 + lane : op_bytes, 0, 0);
       }
     }
+  }
+  u32x4 bv[KPW][NT];
+  uint32_t sword[KPW][NP];
+#pragma unroll
+  for (int i = 0; i < KPW; ++i) {
+    const int ks = S0 + wk * KPW + i;
+    const bool step_ok = ks < S1;
+    const bool ok = step_ok && (ks * 128 + kc * 32 < K);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int g = g0 + nt;
-      const uint4 *bp = (const uint4 *)(Bw + (size_t)g * b_group_stride + (size_t)ks * 1024) + lane;
-      bv[i][nt] = valid ? *bp : make_uint4(0, 0, 0, 0);
-      const uint32_t *sp =
-          (const uint32_t *)(Bs + (size_t)(g >> 1) * s_block_stride + (size_t)(ks >> 1) * 256) + lane;
-      uint32_t word = *sp;
-      uint32_t sel = (uint32_t)((g & 1) | ((ks & 1) << 1));
-      sw[i][nt] = valid ? ((word >> (8 * sel)) & 0xFFu) : 127u;
+      const int off = ok ? (gw + nt) * K * 8 + ks * 1024 + lane * 16 : b_bytes;
+      bv[i][nt] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, off, 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int g = gw + 2 * p;
+      const int off = step_ok ? (g >> 1) * gp * 32 + (ks >> 1) * 256 + lane * 4 : s_bytes;
+      sword[i][p] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, off, 0, 0);
     }
   }
 
-  // Phase 2: quantize A in registers and accumulate.
+  // Phase 2: quantize the staged A blocks into LDS.
+  if constexpr (!PREQ) {
+#pragma unroll
+    for (int u = 0; u < UPW; ++u) {
+      const int unit = wave + u * WAVES;
+      if (UPW * WAVES == UNITS || unit < UNITS) {
+        uint32_t s;
+        const uint32_t d = quant_quarter(aw[u], sw_quant, &s);
+        a_lds[unit * 64 + lane] = d;
+        if ((lane & 3) == 0) s_lds[(unit >> 2) * 64 + (unit & 3) * 16 + (lane >> 2)] = (uint8_t)s;
+      }
+    }
+    __syncthreads();
+  }
+
+  // Phase 3: accumulate.
   v4f acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = v4f{0.f, 0.f, 0.f, 0.f};
-
 #pragma unroll
   for (int i = 0; i < KPW; ++i) {
-    if (ks_begin + i >= ks_end) break;
-    const int kel = (ks_begin + i) * 128 + kc * 32;
-    const bool valid = kel < K;
+    const int st = wk * KPW + i;
+    const int ks = S0 + st;
+    uint32_t sb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int g = gw + nt;
+      const uint32_t sel = (uint32_t)((g & 1) | ((ks & 1) << 1));
+      sb[nt] = (sword[i][nt >> 1] >> (8 * sel)) & 0xFFu;
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      uint32_t q[4];
-      uint32_t sa = quant_group32<SW>(aw[i][mt], q);
-      sa = valid ? sa : 127u;
-      v8i a_op = {(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
+      const int blk = st * MT + mt;
+      u32x4 a;
+      uint32_t sa;
+      if constexpr (PREQ) {
+        a = ap[i][mt];
+        sa = asb[i][mt];
+      } else {
+        a = *(const u32x4 *)(a_lds + blk * 256 + lane * 4);
+        sa = s_lds[blk * 64 + lane];
+      }
+      const v8i a_op = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        uint4 b = bv[i][nt];
-        v8i b_op = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_op, b_op, acc[mt][nt], 4, 4, 0, (int)sa,
-                                                                       0, (int)sw[i][nt]);
+        const u32x4 b = bv[i][nt];
+        const v8i b_op = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+        acc[mt][nt] =
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_op, b_op, acc[mt][nt], 4, 4, 0, (int)sa, 0, (int)sb[nt]);
       }
     }
   }
 
-  // Reduce the waves' accumulators through LDS.  Accumulator element r of
-  // lane l in subtile (mt, nt) is C row 16*mt + 4*(l/16) + r, column
-  // 16*nt + l%16.
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave][(mt * NT + nt) * 4 + r][lane] = acc[mt][nt][r];
-  __syncthreads();
-
+  // Epilogue.  Accumulator element r of lane l in subtile (mt, nt) is C row
+  // 16*mt + 4*(l/16) + r, column 16*nt + l%16.  Tile element index
+  // e = (((mt*WN + wn)*NT + nt)*4 + r)*64 + l.
   const int tile = m_tile * n_tiles + n_tile;
-  if (split == 1) {
+  auto store_c = [&](int e, float v) {
+    const int ln = e & 63, i = e >> 6;
+    const int r = i & 3, t = i >> 2;  // t = mt*TN + (wn*NT + nt)
+    const int mt = t / TN, sub = t % TN;
+    const int row = m0 + 16 * mt + 4 * (ln >> 4) + r;
+    const int col = 16 * (n_tile * TN + sub) + (ln & 15);
+    if (row < M) C[(size_t)row * N + col] = (uint16_t)f32_to_bf16_rne(v);
+  };
+  auto elem = [&](int mt, int nt, int r) { return (((mt * WN + wn) * NT + nt) * 4 + r) * 64 + lane; };
+
+  if constexpr (WK == 1) {
+    if (split == 1) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) store_c(elem(mt, nt, r), acc[mt][nt][r]);
+      return;
+    }
+  } else {
+    // add the WK waves of each column group in wave order
+    __syncthreads();  // LDS is reused
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wk * E + elem(mt, nt, r)] = acc[mt][nt][r];
+    __syncthreads();
+    if (split == 1) {
+      for (int e = threadIdx.x; e < E; e += NTH) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < WK; ++w) s += red[w * E + e];
+        store_c(e, s);
+      }
+      return;
+    }
+  }
+
+  // Split K across workgroups.  Each writes its partial tile to its own slot
+  // with device-coherent stores, waits until they have completed, and takes
+  // a ticket; the workgroup that draws the last ticket reads every slot with
+  // device-coherent loads, adds them in slot order and stores C.  Only these
+  // accesses touch the workspace, so no cache-wide write-back is needed.
+  float *mine = partials + ((size_t)tile * split + sk) * E;
+  if constexpr (WK == 1) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __hip_atomic_store(mine + elem(mt, nt, r), acc[mt][nt][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
     for (int e = threadIdx.x; e < E; e += NTH) {
-      const int i = e >> 6, ln = e & 63;
       float s = 0.f;
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) s += red[w][i][ln];
-      const int mt = i / (4 * NT), nt = (i >> 2) % NT, r = i & 3;
-      const int row = m0 + 16 * mt + 4 * (ln >> 4) + r;
-      const int col = 16 * (g0 + nt) + (ln & 15);
-      if (row < M) C[(size_t)row * N + col] = (uint16_t)f32_to_bf16_rne(s);
+      for (int w = 0; w < WK; ++w) s += red[w * E + e];
+      __hip_atomic_store(mine + e, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    return;
   }
-
-  float *mine = partials + ((size_t)tile * split + sk) * E;
-  for (int e = threadIdx.x; e < E; e += NTH) {
-    const int i = e >> 6, ln = e & 63;
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) s += red[w][i][ln];
-    mine[e] = s;
-  }
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's slot stores have completed
   __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(&tickets[tile], 1u) == (uint32_t)(split - 1)) ? 1u : 0u;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(&tickets[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     (uint32_t)(split - 1)
+                 ? 1u
+                 : 0u;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   const float *all = partials + (size_t)tile * split * E;
   for (int e = threadIdx.x; e < E; e += NTH) {
     float s = 0.f;
-    for (int j = 0; j < split; ++j) s += __builtin_nontemporal_load(all + (size_t)j * E + e);
-    const int i = e >> 6, ln = e & 63;
-    const int mt = i / (4 * NT), nt = (i >> 2) % NT, r = i & 3;
-    const int row = m0 + 16 * mt + 4 * (ln >> 4) + r;
-    const int col = 16 * (g0 + nt) + (ln & 15);
-    if (row < M) C[(size_t)row * N + col] = (uint16_t)f32_to_bf16_rne(s);
+    for (int j = 0; j < split; ++j)
+      s += __hip_atomic_load(all + (size_t)j * E + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    store_c(e, s);
   }
-  if (threadIdx.x == 0) tickets[tile] = 0u;
+  if (threadIdx.x == 0) __hip_atomic_store(&tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// A quantized once into operand blocks for the pre-quantized mode: block
+// (m tile, step) holds 1 KiB of codes (operand lane L's 16 bytes at 16*L)
+// and 64 scale bytes.  One wave per 16 rows x 32 elements, four consecutive
+// lanes per group, as in the staging of the fused mode.
+__global__ __launch_bounds__(256) void quant_operand_kernel(const uint16_t *__restrict__ A, uint8_t *__restrict__ Aop,
+                                                            int M, int K, int units, int sw_quant) {
+  const int lane = threadIdx.x & 63;
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);  // (m tile, step, chunk), chunk fastest
+  if (unit >= units) return;
+  const int KS = (K + 127) >> 7;
+  const int ch = unit & 3;
+  const int ks = (unit >> 2) % KS;
+  const int mtile = (unit >> 2) / KS;
+  const int row = mtile * 16 + (lane >> 2);
+  const int kel = ks * 128 + ch * 32 + (lane & 3) * 8;
+  const int a_bytes = M * K * 2;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, a_bytes, kRsrcWord3);
+  const bool ok = (row < M) && (ks * 128 + ch * 32 < K);
+  const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ok ? (row * K + kel) * 2 : a_bytes, 0, 0);
+  uint32_t s;
+  const uint32_t d = quant_quarter(w, sw_quant, &s);
+  uint8_t *blk = Aop + (size_t)(mtile * KS + ks) * 1088;
+  ((uint32_t *)blk)[ch * 64 + lane] = d;
+  if ((lane & 3) == 0) blk[1024 + ch * 16 + (lane >> 2)] = (uint8_t)s;
+}
+
+// Pre-quantized A, long K: a K loop instead of a fully unrolled run.
+// The workgroup owns 16*MW rows x 16*NW*WN columns over the whole K range
+// (or a split of it); its WN waves own NW subtiles each.  Per 128-wide step
+// the workgroup copies the MW operand blocks of A (1088 bytes each) into one
+// of two LDS stages, all waves read them from there, and each wave streams
+// its own B operands from memory, P steps ahead in registers.
+template <int MW, int NW, int WN, int P>
+__global__ __launch_bounds__(64 * WN) void gemm_loop_kernel(const uint8_t *__restrict__ Aop,
+                                                           const uint8_t *__restrict__ Bw,
+                                                           const uint8_t *__restrict__ Bs, uint16_t *__restrict__ C,
+                                                           float *__restrict__ partials,
+                                                           uint32_t *__restrict__ tickets, int M, int N, int K,
+                                                           int split, int n_tiles) {
+  constexpr int NTH = 64 * WN;
+  constexpr int TN = NW * WN;
+  constexpr int E = MW * TN * 256;
+  constexpr int NP = (NW + 1) / 2;
+  constexpr int STAGE = MW * 1088;                  // bytes of A per step
+  constexpr int CHUNKS = STAGE / 16;                // 16-byte pieces per step
+  constexpr int CPT = (CHUNKS + NTH - 1) / NTH;     // pieces per thread
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][STAGE];
+  __shared__ uint32_t s_last;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int bid = blockIdx.x;
+  const int n_tile = bid % n_tiles;
+  const int rest = bid / n_tiles;
+  const int sk = rest % split;
+  const int m_tile = rest / split;
+  const int mb0 = m_tile * MW;  // first 16-row operand block row
+  const int gw = n_tile * TN + wave * NW;
+  const int kc = lane >> 4;
+
+  const int KS = (K + 127) >> 7;
+  const int S0 = (int)((uint32_t)(sk * KS) / (uint32_t)split);
+  const int S1 = (int)((uint32_t)((sk + 1) * KS) / (uint32_t)split);
+  const int gp = ((K >> 5) + 7) & ~7;
+  const int mblocks = (M + 15) >> 4;
+  const int op_bytes = mblocks * KS * 1088;
+  const int b_bytes = (N >> 4) * K * 8;
+  const int s_bytes = ((N + 255) >> 8) * 8 * gp * 32;
+  const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Aop, 0, op_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Bw, 0, b_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Bs, 0, s_bytes, kRsrcWord3);
+
+  // A pieces of step ks this thread copies: piece c of block mw sits at
+  // byte 16*c of that block; blocks past M or steps past the run read zeros.
+  auto load_a = [&](int ks, u32x4 (&v)[CPT]) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int piece = threadIdx.x + j * NTH;
+      const int mw = piece / 68, c = piece % 68;
+      const int mb = mb0 + mw;
+      const bool ok = piece < CHUNKS && ks < S1 && mb < mblocks;
+      v[j] = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, ok ? (mb * KS + ks) * 1088 + c * 16 : op_bytes, 0, 0);
+    }
+  };
+  auto load_b = [&](int ks, u32x4 (&bv)[NW], uint32_t (&sw)[NP]) {
+    const bool step_ok = ks < S1;
+    const bool ok = step_ok && (ks * 128 + kc * 32 < K);
+#pragma unroll
+    for (int nt = 0; nt < NW; ++nt)
+      bv[nt] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, ok ? (gw + nt) * K * 8 + ks * 1024 + lane * 16 : b_bytes,
+                                                      0, 0);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int g = gw + 2 * p;
+      sw[p] = __builtin_amdgcn_raw_buffer_load_b32(
+          s_rsrc, step_ok ? (g >> 1) * gp * 32 + (ks >> 1) * 256 + lane * 4 : s_bytes, 0, 0);
+    }
+  };
+
+  v4f acc[MW][NW];
+#pragma unroll
+  for (int mw = 0; mw < MW; ++mw)
+#pragma unroll
+    for (int nt = 0; nt < NW; ++nt) acc[mw][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 av[P][CPT];
+  u32x4 bv[P][NW];
+  uint32_t sw[P][NP];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    load_a(S0 + p, av[p]);
+    load_b(S0 + p, bv[p], sw[p]);
+  }
+
+  const int iters = (S1 - S0 + P - 1) / P;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int ks = S0 + it * P + p;
+      const int buf = p & 1;
+      // stage A of this step
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int piece = threadIdx.x + j * NTH;
+        if (CPT * NTH == CHUNKS || piece < CHUNKS) *(u32x4 *)(a_lds[buf] + piece * 16) = av[p][j];
+      }
+      __syncthreads();
+      // refill this slot with the step P ahead
+      load_a(ks + P, av[p]);
+      u32x4 b[NW];
+      uint32_t sc[NP];
+#pragma unroll
+      for (int nt = 0; nt < NW; ++nt) b[nt] = bv[p][nt];
+#pragma unroll
+      for (int q = 0; q < NP; ++q) sc[q] = sw[p][q];
+      load_b(ks + P, bv[p], sw[p]);
+#pragma unroll
+      for (int mw = 0; mw < MW; ++mw) {
+        const u32x4 a = *(const u32x4 *)(a_lds[buf] + mw * 1088 + lane * 16);
+        const uint32_t sa = a_lds[buf][mw * 1088 + 1024 + lane];
+        const v8i a_op = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+#pragma unroll
+        for (int nt = 0; nt < NW; ++nt) {
+          const int g = gw + nt;
+          const uint32_t sel = (uint32_t)((g & 1) | ((ks & 1) << 1));
+          const uint32_t sb = (sc[nt >> 1] >> (8 * sel)) & 0xFFu;
+          const v8i b_op = {(int)b[nt].x, (int)b[nt].y, (int)b[nt].z, (int)b[nt].w, 0, 0, 0, 0};
+          acc[mw][nt] =
+              __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_op, b_op, acc[mw][nt], 4, 4, 0, (int)sa, 0, (int)sb);
+        }
+      }
+    }
+  }
+
+  // Epilogue: accumulator element r of lane l in subtile (mw, nt) is C row
+  // 16*mw + 4*(l/16) + r, column 16*nt + l%16.
+  const int m0 = mb0 * 16;
+  const int tile = m_tile * n_tiles + n_tile;
+  auto col_of = [&](int nt) { return 16 * (gw + nt) + (lane & 15); };
+  if (split == 1) {
+#pragma unroll
+    for (int mw = 0; mw < MW; ++mw)
+#pragma unroll
+      for (int nt = 0; nt < NW; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + 16 * mw + 4 * (lane >> 4) + r;
+          if (row < M) C[(size_t)row * N + col_of(nt)] = (uint16_t)f32_to_bf16_rne(acc[mw][nt][r]);
+        }
+    return;
+  }
+  // split K across workgroups: slots, ticket, last one adds (as in gemm_kernel)
+  auto elem = [&](int mw, int nt, int r) { return (((mw * WN + wave) * NW + nt) * 4 + r) * 64 + lane; };
+  float *mine = partials + ((size_t)tile * split + sk) * E;
+#pragma unroll
+  for (int mw = 0; mw < MW; ++mw)
+#pragma unroll
+    for (int nt = 0; nt < NW; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        __hip_atomic_store(mine + elem(mw, nt, r), acc[mw][nt][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(&tickets[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     (uint32_t)(split - 1)
+                 ? 1u
+                 : 0u;
+  __syncthreads();
+  if (!s_last) return;
+  const float *all = partials + (size_t)tile * split * E;
+#pragma unroll
+  for (int mw = 0; mw < MW; ++mw)
+#pragma unroll
+    for (int nt = 0; nt < NW; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = 0.f;
+        for (int j = 0; j < split; ++j)
+          v += __hip_atomic_load(all + (size_t)j * E + elem(mw, nt, r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int row = m0 + 16 * mw + 4 * (lane >> 4) + r;
+        if (row < M) C[(size_t)row * N + col_of(nt)] = (uint16_t)f32_to_bf16_rne(v);
+      }
+  if (threadIdx.x == 0) __hip_atomic_store(&tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+size_t operand_a_bytes(int M, int K) { return (size_t)((M + 15) / 16) * (size_t)((K + 127) / 128) * 1088; }
 
 // ---------------------------------------------------------------- table
 
-typedef hipError_t (*launch_fn)(const GemmArgs &, int split, hipStream_t);
+typedef hipError_t (*launch_fn)(const GemmArgs &, int split, bool sw, hipStream_t);
 
-template <int MT, int NT, int KPW, int WAVES, bool SW>
-static hipError_t launch_variant(const GemmArgs &a, int split, hipStream_t stream) {
-  const int n_tiles = a.N / (16 * NT);
+template <int MT, int NT, int WN, int WK, int KPW, bool PREQ>
+static hipError_t launch_variant(const GemmArgs &a, int split, bool sw, hipStream_t stream) {
+  const int n_tiles = a.N / (16 * NT * WN);
   const int m_tiles = (a.M + 16 * MT - 1) / (16 * MT);
-  const int tiles = n_tiles * m_tiles;
-  uint32_t *tickets = (uint32_t *)a.workspace;
-  float *partials = (float *)((char *)a.workspace + kTicketBytes);
-  dim3 grid((unsigned)(tiles * split));
-  gemm_fused_kernel<MT, NT, KPW, WAVES, SW><<<grid, 64 * WAVES, 0, stream>>>(
-      (const uint16_t *)a.A, (const uint8_t *)a.Bw, (const uint8_t *)a.Bs, (uint16_t *)a.C, partials, tickets, a.M,
-      a.N, a.K, split, n_tiles);
+  char *ws = (char *)a.workspace;
+  uint8_t *aop = nullptr;
+  if (PREQ) {
+    aop = (uint8_t *)(ws + kTicketBytes);
+    const int units = ((a.M + 15) / 16) * ((a.K + 127) / 128) * 4;
+    quant_operand_kernel<<<(units + 3) / 4, 256, 0, stream>>>((const uint16_t *)a.A, aop, a.M, a.K, units, sw ? 1 : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  uint32_t *tickets = (uint32_t *)ws;
+  float *partials = nullptr;
+  if (split > 1)
+    partials = (float *)(ws + kTicketBytes + (PREQ ? ((operand_a_bytes(a.M, a.K) + 255) & ~(size_t)255) : 0));
+  dim3 grid((unsigned)(n_tiles * m_tiles * split));
+  gemm_kernel<MT, NT, WN, WK, KPW, PREQ><<<grid, 64 * WN * WK, 0, stream>>>(
+      (const uint16_t *)a.A, aop, (const uint8_t *)a.Bw, (const uint8_t *)a.Bs, (uint16_t *)a.C, partials, tickets, a.M,
+      a.N, a.K, split, n_tiles, sw ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <int MW, int NW, int WN, int P>
+static hipError_t launch_loop_variant(const GemmArgs &a, int split, bool sw, hipStream_t stream) {
+  const int n_tiles = a.N / (16 * NW * WN);
+  const int m_tiles = (a.M + 16 * MW - 1) / (16 * MW);
+  char *ws = (char *)a.workspace;
+  uint8_t *aop = (uint8_t *)(ws + kTicketBytes);
+  const int units = ((a.M + 15) / 16) * ((a.K + 127) / 128) * 4;
+  quant_operand_kernel<<<(units + 3) / 4, 256, 0, stream>>>((const uint16_t *)a.A, aop, a.M, a.K, units, sw ? 1 : 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  uint32_t *tickets = (uint32_t *)ws;
+  float *partials =
+      split > 1 ? (float *)(ws + kTicketBytes + ((operand_a_bytes(a.M, a.K) + 255) & ~(size_t)255)) : nullptr;
+  dim3 grid((unsigned)(n_tiles * m_tiles * split));
+  gemm_loop_kernel<MW, NW, WN, P><<<grid, 64 * WN, 0, stream>>>(aop, (const uint8_t *)a.Bw, (const uint8_t *)a.Bs,
+                                                                 (uint16_t *)a.C, partials, tickets, a.M, a.N, a.K,
+                                                                 split, n_tiles);
   return hipGetLastError();
 }
 
 struct Variant {
-  int mt, nt, kpw, waves;
-  launch_fn hw, sw;
+  int mt, nt, wn, wk, kpw, pq;
+  launch_fn fn;
 };
 
-#define MXFP4_VARIANT(MT, NT, KPW, WAVES) \
-  {MT, NT, KPW, WAVES, launch_variant<MT, NT, KPW, WAVES, false>, launch_variant<MT, NT, KPW, WAVES, true>}
+#define V(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 0, launch_variant<MT, NT, WN, WK, KPW, false>}
+#define VQ(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 1, launch_variant<MT, NT, WN, WK, KPW, true>}
+// K-loop kernels (pre-quantized A) are listed with wk = 0 and kpw = the
+// prefetch depth P: they cover any K
+#define VL(MW, NW, WN, P) {MW, NW, WN, 0, P, 1, launch_loop_variant<MW, NW, WN, P>}
 
 static const Variant kVariants[] = {
-    MXFP4_VARIANT(1, 2, 1, 4), MXFP4_VARIANT(1, 2, 2, 4), MXFP4_VARIANT(1, 2, 4, 4), MXFP4_VARIANT(1, 2, 8, 4),
-    MXFP4_VARIANT(2, 2, 1, 4), MXFP4_VARIANT(2, 2, 2, 4), MXFP4_VARIANT(2, 2, 4, 4), MXFP4_VARIANT(2, 2, 8, 4),
-    MXFP4_VARIANT(4, 2, 1, 4), MXFP4_VARIANT(4, 2, 2, 4), MXFP4_VARIANT(4, 2, 4, 4), MXFP4_VARIANT(4, 2, 8, 4),
+    VL(4, 1, 4, 8), VL(4, 1, 4, 16), VL(4, 1, 2, 8), VL(4, 1, 2, 16), VL(4, 2, 4, 8), VL(4, 1, 8, 8),
+    VL(4, 1, 8, 16), VL(4, 1, 7, 8), VL(4, 1, 7, 16), VL(8, 1, 4, 8), VL(8, 1, 2, 8), VL(2, 1, 8, 8),
+    VL(2, 1, 8, 16), VL(4, 2, 2, 8),
+    VL(2, 1, 1, 2), VL(2, 1, 1, 4), VL(2, 1, 2, 2), VL(2, 1, 2, 4), VL(2, 1, 4, 2), VL(2, 1, 4, 4),
+    VL(2, 1, 7, 2), VL(2, 1, 7, 4), VL(2, 1, 8, 2), VL(2, 1, 8, 4), VL(2, 2, 1, 2), VL(2, 2, 1, 4),
+    VL(2, 2, 2, 2), VL(2, 2, 2, 4), VL(2, 2, 4, 2), VL(2, 2, 4, 4), VL(2, 2, 7, 2), VL(2, 2, 7, 4),
+    VL(2, 2, 8, 2), VL(2, 2, 8, 4), VL(2, 4, 1, 2), VL(2, 4, 1, 4), VL(2, 4, 2, 2), VL(2, 4, 2, 4),
+    VL(2, 4, 4, 2), VL(2, 4, 4, 4), VL(2, 4, 7, 2), VL(2, 4, 7, 4), VL(2, 4, 8, 2), VL(2, 4, 8, 4),
+    VL(4, 1, 1, 2), VL(4, 1, 1, 4), VL(4, 1, 2, 2), VL(4, 1, 2, 4), VL(4, 1, 4, 2), VL(4, 1, 4, 4),
+    VL(4, 1, 7, 2), VL(4, 1, 7, 4), VL(4, 1, 8, 2), VL(4, 1, 8, 4), VL(4, 2, 1, 2), VL(4, 2, 1, 4),
+    VL(4, 2, 2, 2), VL(4, 2, 2, 4), VL(4, 2, 4, 2), VL(4, 2, 4, 4), VL(4, 2, 7, 2), VL(4, 2, 7, 4),
+    VL(4, 2, 8, 2), VL(4, 2, 8, 4), VL(4, 4, 1, 2), VL(4, 4, 1, 4), VL(4, 4, 2, 2), VL(4, 4, 2, 4),
+    VL(4, 4, 4, 2), VL(4, 4, 4, 4), VL(4, 4, 7, 2), VL(4, 4, 7, 4), VL(4, 4, 8, 2), VL(4, 4, 8, 4),
+    VL(8, 1, 1, 2), VL(8, 1, 1, 4), VL(8, 1, 2, 2), VL(8, 1, 2, 4), VL(8, 1, 4, 2), VL(8, 1, 4, 4),
+    VL(8, 1, 7, 2), VL(8, 1, 7, 4), VL(8, 1, 8, 2), VL(8, 1, 8, 4), VL(8, 2, 1, 2), VL(8, 2, 1, 4),
+    VL(8, 2, 2, 2), VL(8, 2, 2, 4), VL(8, 2, 4, 2), VL(8, 2, 4, 4), VL(8, 2, 7, 2), VL(8, 2, 7, 4),
+    VL(8, 2, 8, 2), VL(8, 2, 8, 4), VL(8, 4, 1, 2), VL(8, 4, 2, 2), VL(8, 4, 4, 2), VL(8, 4, 7, 2),
+    VL(8, 4, 8, 2),
+    V(1, 1, 1, 1, 1), V(1, 1, 1, 1, 2), V(1, 1, 1, 1, 4), V(1, 1, 1, 2, 1), V(1, 1, 1, 2, 2), V(1, 1, 1, 2, 4),
+    V(1, 1, 1, 4, 1), V(1, 1, 1, 4, 2), V(1, 1, 1, 4, 4), V(1, 1, 1, 8, 1), V(1, 1, 1, 8, 2), V(1, 1, 1, 8, 4),
+    V(1, 1, 1, 16, 1), V(1, 1, 1, 16, 2), V(1, 1, 2, 1, 1), V(1, 1, 2, 1, 2), V(1, 1, 2, 1, 4), V(1, 1, 2, 2, 1),
+    V(1, 1, 2, 2, 2), V(1, 1, 2, 2, 4), V(1, 1, 2, 4, 1), V(1, 1, 2, 4, 2), V(1, 1, 2, 4, 4), V(1, 1, 2, 8, 1),
+    V(1, 1, 2, 8, 2), V(1, 1, 2, 8, 4), V(1, 1, 4, 1, 1), V(1, 1, 4, 1, 2), V(1, 1, 4, 1, 4), V(1, 1, 4, 2, 1),
+    V(1, 1, 4, 2, 2), V(1, 1, 4, 2, 4), V(1, 1, 4, 4, 1), V(1, 1, 4, 4, 2), V(1, 1, 4, 4, 4), V(1, 2, 1, 1, 1),
+    V(1, 2, 1, 1, 2), V(1, 2, 1, 1, 4), V(1, 2, 1, 2, 1), V(1, 2, 1, 2, 2), V(1, 2, 1, 2, 4), V(1, 2, 1, 4, 1),
+    V(1, 2, 1, 4, 2), V(1, 2, 1, 4, 4), V(1, 2, 1, 8, 1), V(1, 2, 1, 8, 2), V(1, 2, 1, 8, 4), V(1, 2, 1, 16, 1),
+    V(1, 2, 1, 16, 2), V(1, 2, 2, 1, 1), V(1, 2, 2, 1, 2), V(1, 2, 2, 1, 4), V(1, 2, 2, 2, 1), V(1, 2, 2, 2, 2),
+    V(1, 2, 2, 2, 4), V(1, 2, 2, 4, 1), V(1, 2, 2, 4, 2), V(1, 2, 2, 4, 4), V(1, 2, 2, 8, 1), V(1, 2, 2, 8, 2),
+    V(1, 2, 2, 8, 4), V(1, 2, 4, 1, 1), V(1, 2, 4, 1, 2), V(1, 2, 4, 1, 4), V(1, 2, 4, 2, 1), V(1, 2, 4, 2, 2),
+    V(1, 2, 4, 2, 4), V(1, 2, 4, 4, 1), V(1, 2, 4, 4, 2), V(1, 2, 4, 4, 4), V(2, 1, 1, 1, 1), V(2, 1, 1, 1, 2),
+    V(2, 1, 1, 2, 1), V(2, 1, 1, 2, 2), V(2, 1, 1, 4, 1), V(2, 1, 1, 4, 2), V(2, 1, 1, 8, 1), V(2, 1, 1, 8, 2),
+    V(2, 1, 2, 1, 1), V(2, 1, 2, 1, 2), V(2, 1, 2, 2, 1), V(2, 1, 2, 2, 2), V(2, 1, 2, 4, 1), V(2, 1, 2, 4, 2),
+    V(2, 1, 2, 8, 1), V(2, 1, 2, 8, 2), V(2, 1, 4, 1, 1), V(2, 1, 4, 1, 2), V(2, 1, 4, 2, 1), V(2, 1, 4, 2, 2),
+    V(2, 1, 4, 4, 1), V(2, 1, 4, 4, 2), V(2, 2, 1, 1, 1), V(2, 2, 1, 1, 2), V(2, 2, 1, 2, 1), V(2, 2, 1, 2, 2),
+    V(2, 2, 1, 4, 1), V(2, 2, 1, 4, 2), V(2, 2, 1, 8, 1), V(2, 2, 1, 8, 2), V(2, 2, 2, 1, 1), V(2, 2, 2, 1, 2),
+    V(2, 2, 2, 2, 1), V(2, 2, 2, 2, 2), V(2, 2, 2, 4, 1), V(2, 2, 2, 4, 2), V(2, 2, 4, 1, 1), V(2, 2, 4, 1, 2),
+    V(2, 2, 4, 2, 1), V(2, 2, 4, 2, 2), V(4, 1, 1, 1, 1), V(4, 1, 1, 1, 2), V(4, 1, 1, 2, 1), V(4, 1, 1, 2, 2),
+    V(4, 1, 1, 4, 1), V(4, 1, 1, 4, 2), V(4, 1, 2, 1, 1), V(4, 1, 2, 1, 2), V(4, 1, 2, 2, 1), V(4, 1, 2, 2, 2),
+    V(4, 1, 2, 4, 1), V(4, 1, 2, 4, 2), V(4, 1, 4, 1, 1), V(4, 1, 4, 1, 2), V(4, 1, 4, 2, 1), V(4, 1, 4, 2, 2),
+    V(4, 1, 8, 1, 1), V(4, 1, 8, 1, 2), V(4, 2, 1, 1, 1), V(4, 2, 1, 1, 2), V(4, 2, 1, 2, 1), V(4, 2, 1, 2, 2),
+    V(4, 2, 1, 4, 1), V(4, 2, 1, 4, 2), V(4, 2, 2, 1, 1), V(4, 2, 2, 1, 2), V(4, 2, 2, 2, 1), V(4, 2, 2, 2, 2),
+    V(4, 2, 4, 1, 1), V(4, 2, 4, 1, 2), V(4, 2, 8, 1, 1), V(4, 2, 8, 1, 2), VQ(1, 1, 1, 1, 1), VQ(1, 1, 1, 1, 2),
+    VQ(1, 1, 1, 1, 4), VQ(1, 1, 1, 4, 1), VQ(1, 1, 1, 4, 2), VQ(1, 1, 1, 4, 4), VQ(1, 1, 1, 8, 1), VQ(1, 1, 1, 8, 2),
+    VQ(1, 1, 1, 8, 4), VQ(1, 1, 1, 16, 1), VQ(1, 1, 1, 16, 2), VQ(1, 1, 1, 16, 4), VQ(1, 1, 2, 1, 1), VQ(1, 1, 2, 1, 2),
+    VQ(1, 1, 2, 1, 4), VQ(1, 1, 2, 4, 1), VQ(1, 1, 2, 4, 2), VQ(1, 1, 2, 4, 4), VQ(1, 1, 2, 8, 1), VQ(1, 1, 2, 8, 2),
+    VQ(1, 1, 2, 8, 4), VQ(1, 2, 1, 1, 1), VQ(1, 2, 1, 1, 2), VQ(1, 2, 1, 1, 4), VQ(1, 2, 1, 4, 1), VQ(1, 2, 1, 4, 2),
+    VQ(1, 2, 1, 4, 4), VQ(1, 2, 1, 8, 1), VQ(1, 2, 1, 8, 2), VQ(1, 2, 1, 8, 4), VQ(1, 2, 1, 16, 1), VQ(1, 2, 1, 16, 2),
+    VQ(1, 2, 1, 16, 4), VQ(1, 2, 2, 1, 1), VQ(1, 2, 2, 1, 2), VQ(1, 2, 2, 1, 4), VQ(1, 2, 2, 4, 1), VQ(1, 2, 2, 4, 2),
+    VQ(1, 2, 2, 4, 4), VQ(1, 2, 2, 8, 1), VQ(1, 2, 2, 8, 2), VQ(1, 2, 2, 8, 4), VQ(2, 1, 1, 1, 1), VQ(2, 1, 1, 1, 2),
+    VQ(2, 1, 1, 1, 4), VQ(2, 1, 1, 4, 1), VQ(2, 1, 1, 4, 2), VQ(2, 1, 1, 4, 4), VQ(2, 1, 1, 8, 1), VQ(2, 1, 1, 8, 2),
+    VQ(2, 1, 1, 8, 4), VQ(2, 1, 2, 1, 1), VQ(2, 1, 2, 1, 2), VQ(2, 1, 2, 1, 4), VQ(2, 1, 2, 4, 1), VQ(2, 1, 2, 4, 2),
+    VQ(2, 1, 2, 4, 4), VQ(2, 1, 2, 8, 1), VQ(2, 1, 2, 8, 2), VQ(2, 1, 2, 8, 4), VQ(2, 2, 1, 1, 1), VQ(2, 2, 1, 1, 2),
+    VQ(2, 2, 1, 1, 4), VQ(2, 2, 1, 4, 1), VQ(2, 2, 1, 4, 2), VQ(2, 2, 1, 4, 4), VQ(2, 2, 1, 8, 1), VQ(2, 2, 1, 8, 2),
+    VQ(2, 2, 1, 8, 4), VQ(2, 2, 2, 1, 1), VQ(2, 2, 2, 1, 2), VQ(2, 2, 2, 1, 4), VQ(2, 2, 2, 4, 1), VQ(2, 2, 2, 4, 2),
+    VQ(2, 2, 2, 4, 4), VQ(4, 1, 1, 1, 1), VQ(4, 1, 1, 1, 2), VQ(4, 1, 1, 1, 4), VQ(4, 1, 1, 2, 1), VQ(4, 1, 1, 2, 2),
+    VQ(4, 1, 1, 2, 4), VQ(4, 1, 1, 4, 1), VQ(4, 1, 1, 4, 2), VQ(4, 1, 1, 4, 4), VQ(4, 1, 1, 8, 1), VQ(4, 1, 1, 8, 2),
+    VQ(4, 1, 1, 8, 4), VQ(4, 1, 2, 1, 1), VQ(4, 1, 2, 1, 2), VQ(4, 1, 2, 1, 4), VQ(4, 1, 2, 2, 1), VQ(4, 1, 2, 2, 2),
+    VQ(4, 1, 2, 2, 4), VQ(4, 1, 2, 4, 1), VQ(4, 1, 2, 4, 2), VQ(4, 1, 2, 4, 4), VQ(4, 1, 4, 1, 1), VQ(4, 1, 4, 1, 2),
+    VQ(4, 1, 4, 1, 4), VQ(4, 1, 4, 2, 1), VQ(4, 1, 4, 2, 2), VQ(4, 1, 4, 2, 4), VQ(4, 2, 1, 1, 1), VQ(4, 2, 1, 1, 2),
+    VQ(4, 2, 1, 1, 4), VQ(4, 2, 1, 2, 1), VQ(4, 2, 1, 2, 2), VQ(4, 2, 1, 2, 4), VQ(4, 2, 1, 4, 1), VQ(4, 2, 1, 4, 2),
+    VQ(4, 2, 1, 4, 4), VQ(4, 2, 2, 1, 1), VQ(4, 2, 2, 1, 2), VQ(4, 2, 2, 1, 4), VQ(4, 2, 2, 2, 1), VQ(4, 2, 2, 2, 2),
+    VQ(4, 2, 2, 2, 4), VQ(4, 2, 4, 1, 1), VQ(4, 2, 4, 1, 2), VQ(4, 2, 4, 1, 4), VQ(4, 4, 1, 1, 1), VQ(4, 4, 1, 1, 2),
+    VQ(4, 4, 1, 1, 4), VQ(4, 4, 1, 2, 1), VQ(4, 4, 1, 2, 2), VQ(4, 4, 1, 2, 4), VQ(4, 4, 2, 1, 1), VQ(4, 4, 2, 1, 2),
+    VQ(4, 4, 2, 1, 4), VQ(4, 4, 4, 1, 1), VQ(4, 4, 4, 1, 2), VQ(4, 4, 4, 1, 4), VQ(8, 1, 1, 1, 1), VQ(8, 1, 1, 1, 2),
+    VQ(8, 1, 1, 1, 4), VQ(8, 1, 1, 2, 1), VQ(8, 1, 1, 2, 2), VQ(8, 1, 1, 2, 4), VQ(8, 1, 1, 4, 1), VQ(8, 1, 1, 4, 2),
+    VQ(8, 1, 1, 4, 4), VQ(8, 1, 2, 1, 1), VQ(8, 1, 2, 1, 2), VQ(8, 1, 2, 1, 4), VQ(8, 1, 2, 2, 1), VQ(8, 1, 2, 2, 2),
+    VQ(8, 1, 2, 2, 4), VQ(8, 2, 1, 1, 1), VQ(8, 2, 1, 1, 2), VQ(8, 2, 1, 1, 4), VQ(8, 2, 1, 2, 1), VQ(8, 2, 1, 2, 2),
+    VQ(8, 2, 1, 2, 4), VQ(8, 2, 2, 1, 1), VQ(8, 2, 2, 1, 2), VQ(8, 2, 2, 1, 4),
 };
+
+#undef V
+#undef VQ
+#undef VL
 
 int num_gemm_variants() { return (int)(sizeof(kVariants) / sizeof(kVariants[0])); }
 
-void gemm_variant_shape(int v, int *mt, int *nt, int *kpw, int *waves) {
-  *mt = kVariants[v].mt;
-  *nt = kVariants[v].nt;
-  *kpw = kVariants[v].kpw;
-  *waves = kVariants[v].waves;
+void gemm_variant_shape(int v, Schedule *s) {
+  s->mt = kVariants[v].mt;
+  s->nt = kVariants[v].nt;
+  s->wn = kVariants[v].wn;
+  s->wk = kVariants[v].wk;
+  s->kpw = kVariants[v].kpw;
+  s->pq = kVariants[v].pq;
+  s->variant = v;
 }
 
-int find_gemm_variant(int mt, int nt, int kpw, int waves) {
+int find_gemm_variant(int mt, int nt, int wn, int wk, int kpw, int pq) {
   for (int v = 0; v < num_gemm_variants(); ++v)
-    if (kVariants[v].mt == mt && kVariants[v].nt == nt && kVariants[v].kpw == kpw && kVariants[v].waves == waves)
+    if (kVariants[v].mt == mt && kVariants[v].nt == nt && kVariants[v].wn == wn && kVariants[v].wk == wk &&
+        kVariants[v].kpw == kpw && kVariants[v].pq == pq)
       return v;
   return -1;
 }
 
 size_t gemm_workspace_bytes(const Schedule &s, int M, int N, int K) {
-  (void)K;
-  if (s.split <= 1) return 0;
-  const size_t tiles = (size_t)(N / (16 * s.nt)) * (size_t)((M + 16 * s.mt - 1) / (16 * s.mt));
-  const size_t e = (size_t)s.mt * s.nt * 256;
-  return kTicketBytes + tiles * (size_t)s.split * e * sizeof(float);
+  if (s.split <= 1 && !s.pq) return 0;
+  size_t bytes = kTicketBytes;
+  if (s.pq) bytes += (operand_a_bytes(M, K) + 255) & ~(size_t)255;
+  if (s.split > 1) {
+    const size_t tiles = (size_t)(N / (16 * s.nt * s.wn)) * (size_t)((M + 16 * s.mt - 1) / (16 * s.mt));
+    const size_t e = (size_t)s.mt * s.nt * s.wn * 256;
+    bytes += tiles * (size_t)s.split * e * sizeof(float);
+  }
+  return bytes;
 }
 
 hipError_t launch_gemm(const Schedule &s, const GemmArgs &a, bool sw_quant, hipStream_t stream) {
-  const Variant &v = kVariants[s.variant];
-  return (sw_quant ? v.sw : v.hw)(a, s.split, stream);
+  return kVariants[s.variant].fn(a, s.split, sw_quant, stream);
 }
 
 }  // namespace mxfp4

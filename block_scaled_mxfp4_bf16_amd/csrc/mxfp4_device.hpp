@@ -13,6 +13,7 @@ namespace mxfp4 {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Scale byte of a group from the largest |x| given as bf16 magnitude bits
 // (15 bits, sign cleared).  The f32 pattern of amax is those bits << 16.
@@ -42,17 +43,18 @@ __device__ __forceinline__ uint32_t amax_mag16(const uint32_t (&w)[16]) {
   return m.x > m.y ? m.x : m.y;
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// Hardware encode: v_cvt_scalef32_pk_fp4_f32 converts two f32 values divided
-// by the power of two whose exponent field is the scale's, and writes the two
-// codes (first operand low nibble) into byte `sel` of the destination
-// (submission 608632, _hw_mxfp4_quant_op, step 3; submission 711914,
-// _mxfp4_quant_tile_hw).  The scale float is built with exponent field s.
+// Hardware encode.  The pages use v_cvt_scalef32_pk_fp4_f32 on two f32
+// values (submission 608632, _hw_mxfp4_quant_op, step 3; submission 711914,
+// _mxfp4_quant_tile_hw): it divides by the power of two whose exponent field
+// is the scale operand's and writes the two codes (first value in the low
+// nibble) into byte `sel` of the destination.  gfx950 also has the bf16-input
+// form, v_cvt_scalef32_pk_fp4_bf16, which takes the packed pair as stored
+// (low half = even element) and so needs no unpacking; bf16 -> f32 is exact,
+// so both forms see the same values.  The scale float is built with
+// exponent field s.
 template <int SEL>
 __device__ __forceinline__ uint32_t cvt_pair_hw(uint32_t old, uint32_t w, float scale) {
-  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, bf16_lo(w), bf16_hi(w), scale, SEL);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(old, __builtin_bit_cast(bf16x2, w), scale, SEL);
 }
 
 // Software encode of one element, written from the rounding rule itself:

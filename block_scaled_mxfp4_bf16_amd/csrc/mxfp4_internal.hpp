@@ -8,14 +8,17 @@
 namespace mxfp4 {
 
 // A GEMM schedule: compile-time tile shape plus the runtime split count.
-//   mt    16-row M tiles per workgroup (the WG covers 16*mt rows)
-//   nt    16-column N subtiles per wave (all waves of a WG share them)
-//   kpw   most 128-wide K steps one wave handles
-//   waves waves per WG; they split the WG's K range and reduce through LDS
-//   split WGs that split K for one output tile; the last to finish adds the
-//         partial sums from the workspace and stores C
+//   mt    16-row M tiles per workgroup (the workgroup covers 16*mt rows)
+//   nt    16-column N subtiles per wave
+//   wn    waves side by side along N; they share the A the workgroup stages
+//   wk    waves that split the workgroup's K run and add through LDS
+//   kpw   128-wide K steps per wave (a workgroup covers wk*kpw steps)
+//   split workgroups that split K for one output tile; the last to finish
+//         adds the partial sums from the workspace and stores C
+//   pq    1: A is quantized once by a separate launch into operand blocks in
+//         the workspace and the GEMM reads those; 0: the GEMM quantizes A
 struct Schedule {
-  int mt, nt, kpw, waves, split;
+  int mt, nt, wn, wk, kpw, split, pq;
   int variant;  // index into the kernel table
 };
 
@@ -37,8 +40,8 @@ struct GemmArgs {
 
 // Kernel table queries (gemm_kernels.hip).
 int num_gemm_variants();
-void gemm_variant_shape(int v, int *mt, int *nt, int *kpw, int *waves);
-int find_gemm_variant(int mt, int nt, int kpw, int waves);
+void gemm_variant_shape(int v, Schedule *s);  // fills everything but split
+int find_gemm_variant(int mt, int nt, int wn, int wk, int kpw, int pq);
 
 size_t gemm_workspace_bytes(const Schedule &s, int M, int N, int K);
 hipError_t launch_gemm(const Schedule &s, const GemmArgs &a, bool sw_quant, hipStream_t stream);

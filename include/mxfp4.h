@@ -159,7 +159,9 @@ MXFP4_API const char *mxfp4_status_string(mxfp4_status_t status);
 
 /* Name of the kernel schedule mxfp4_gemm picks for a shape (thread-local
  * storage, valid until the next call on the thread), e.g.
- * "mt1_nt2_kpw4_w4_split2"; NULL if the shape is unsupported. */
+ * "mt1_nt1_wn2_wk4_kpw1_split2" (16-row M tiles, 16-column subtiles per
+ * wave, waves along N, waves along K, K steps per wave, workgroups per
+ * output tile along K); NULL if the shape is unsupported. */
 MXFP4_API const char *mxfp4_gemm_schedule_name(int64_t M, int64_t N, int64_t K);
 
 /* Process-wide choice of the e2m1 encoder used by mxfp4_quantize and the

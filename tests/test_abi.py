@@ -104,13 +104,13 @@ def test_preshuffle_rejects_bad_arguments(args, code):
 
 def test_schedule_names_and_override():
     name = mx.mxfp4_gemm_schedule_name(16, 3072, 1536)
-    assert re.fullmatch(r"mt\d+_nt\d+_kpw\d+_w\d+_split\d+", name)
+    assert re.fullmatch(r"mt\d+_nt\d+_wn\d+_wk\d+_kpw\d+_split\d+", name)
     assert mx.mxfp4_gemm_schedule_name(16, 3072, 96) is None
     with pytest.raises(RuntimeError):
-        mx.mxfp4_set_schedule_override("mt9_nt9_kpw9_w9_split1")
-    mx.mxfp4_set_schedule_override("mt1_nt2_kpw4_w4_split3")
+        mx.mxfp4_set_schedule_override("mt9_nt9_wn9_wk9_kpw9_split1")
+    mx.mxfp4_set_schedule_override("mt1_nt1_wn2_wk4_kpw1_split3")
     try:
-        assert mx.mxfp4_gemm_schedule_name(16, 3072, 1536) == "mt1_nt2_kpw4_w4_split3"
+        assert mx.mxfp4_gemm_schedule_name(16, 3072, 1536) == "mt1_nt1_wn2_wk4_kpw1_split3"
         # an override that cannot cover K: the shape is unsupported under it
         assert mx.mxfp4_gemm_schedule_name(16, 3072, 7168 * 4) is None
     finally:

@@ -111,9 +111,17 @@ def test_leaderboard_shapes(name):
         assert_close(got[ms, ns], c.ref_sampled(ms, ns), name)
 
 
-SCHEDULES = ["mt1_nt2_kpw1_w4_split1", "mt1_nt2_kpw2_w4_split3", "mt1_nt2_kpw4_w4_split2",
-             "mt1_nt2_kpw8_w4_split1", "mt2_nt2_kpw1_w4_split4", "mt2_nt2_kpw2_w4_split1",
-             "mt4_nt2_kpw1_w4_split5", "mt4_nt2_kpw4_w4_split1", "mt4_nt2_kpw8_w4_split2"]
+# A spread over the compiled kernels: one and many waves along N and K,
+# one and several steps per wave, single- and multi-workgroup K splits.
+SCHEDULES = ["mt1_nt1_wn1_wk1_kpw1_split17", "mt1_nt1_wn1_wk4_kpw1_split5", "mt1_nt2_wn2_wk2_kpw2_split5",
+             "mt1_nt1_wn4_wk4_kpw2_split3", "mt1_nt1_wn1_wk16_kpw2_split1", "mt2_nt1_wn4_wk2_kpw2_split5",
+             "mt2_nt2_wn2_wk4_kpw1_split5", "mt4_nt1_wn8_wk1_kpw2_split9", "mt4_nt2_wn4_wk1_kpw2_split9",
+             "mt4_nt1_wn2_wk4_kpw2_split3", "mt4_nt2_wn1_wk2_kpw2_split5",
+             # A quantized once by its own launch into operand blocks
+             "mt4_nt2_wn2_wk2_kpw4_split3_pq", "mt1_nt1_wn2_wk8_kpw1_split3_pq", "mt8_nt1_wn2_wk2_kpw4_split3_pq",
+             "mt2_nt2_wn1_wk1_kpw4_split5_pq", "mt4_nt4_wn1_wk2_kpw4_split3_pq",
+             # K-loop kernels (pre-quantized A staged through LDS)
+             "mt4_nt2_wn4_wk0_kpw2_split1_pq", "mt8_nt1_wn2_wk0_kpw4_split3_pq", "mt2_nt4_wn1_wk0_kpw2_split2_pq"]
 
 
 @pytest.mark.parametrize("sched", SCHEDULES)
@@ -183,3 +191,20 @@ def test_workspace_reused_across_shapes_with_more_tiles():
     assert_close(first.run(), first.ref(), "first shape")
     assert_close(second.run(), second.ref(), "second shape")
     assert_close(first.run(), first.ref(), "first shape again")
+
+
+@pytest.mark.parametrize("sched", ["mt4_nt1_wn7_wk0_kpw4_split1_pq", "mt8_nt1_wn2_wk0_kpw2_split2_pq"])
+def test_k_loop_kernels_ragged(sched):
+    """K loop with a step count that is not a multiple of the prefetch depth,
+    a half step (K % 128 == 64), and rows past the last full M tile."""
+    torch = torch_cuda()
+    c = make(torch, 70, 224, 1088, seed=9)
+    mx.mxfp4_set_schedule_override(sched)
+    try:
+        assert mx.mxfp4_gemm_schedule_name(c.M, c.N, c.K) == sched
+        got = c.run()
+        again = c.run()
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+    assert np.array_equal(got, again)
+    assert_close(got, c.ref(), sched)
