@@ -85,7 +85,7 @@ __device__ __forceinline__ uint32_t quant_quarter(const u32x4 &w, int sw_quant, 
   return d;
 }
 
-template <int MT, int NT, int WN, int WK, int KPW, bool PREQ>
+template <int MT, int NT, int WN, int WK, int KPW, bool PREQ, int RB>
 __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__restrict__ A,
                                                            const uint8_t *__restrict__ Aop,
                                                            const uint8_t *__restrict__ Bw,
@@ -96,7 +96,10 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
   constexpr int WAVES = WN * WK;
   constexpr int NTH = 64 * WAVES;
   constexpr int KW = WK * KPW;                      // K steps one workgroup covers at most
-  constexpr int UNITS = KW * MT * 4;                // staged A blocks: 16 rows x 32 elements each
+  // staged A blocks: 16 rows x 32 elements each, or (RB == 8, for M <= 8)
+  // 8 rows x 64 elements, so that no load is spent on rows that do not exist
+  constexpr int UPS = RB == 8 ? 2 : 4;              // blocks per (step, m tile)
+  constexpr int UNITS = KW * MT * UPS;
   constexpr int UPW = (UNITS + WAVES - 1) / WAVES;  // per wave
   constexpr int TN = NT * WN;                       // 16-column subtiles per workgroup
   constexpr int E = MT * TN * 256;                  // outputs per tile
@@ -150,12 +153,14 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
   if constexpr (!PREQ) {
 #pragma unroll
     for (int u = 0; u < UPW; ++u) {
-      const int unit = wave + u * WAVES;  // (step, m tile, chunk) with the chunk fastest
-      const int st = unit / (MT * 4);
-      const int mt = (unit >> 2) % MT;
-      const int ch = unit & 3;
+      // (step, m tile, chunk) with the chunk fastest; with one wave per
+      // column group each wave stages exactly the blocks of its own steps
+      const int unit = WN == 1 ? wk * (KPW * MT * UPS) + u : wave + u * WAVES;
+      const int st = unit / (MT * UPS);
+      const int mt = (unit / UPS) % MT;
+      const int ch = RB == 8 ? 2 * (unit & 1) + ((lane >> 2) & 1) : (unit & 3);
       const int ks = S0 + st;
-      const int row = m0 + 16 * mt + (lane >> 2);
+      const int row = m0 + 16 * mt + (RB == 8 ? (lane >> 3) : (lane >> 2));
       const int kel = ks * 128 + ch * 32 + (lane & 3) * 8;
       const bool ok = (unit < UNITS) && (ks < S1) && (row < M) && (ks * 128 + ch * 32 < K);
       aw[u] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ok ? (row * K + kel) * 2 : a_bytes, 0, 0);
@@ -202,15 +207,32 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
   if constexpr (!PREQ) {
 #pragma unroll
     for (int u = 0; u < UPW; ++u) {
-      const int unit = wave + u * WAVES;
+      const int unit = WN == 1 ? wk * (KPW * MT * UPS) + u : wave + u * WAVES;
       if (UPW * WAVES == UNITS || unit < UNITS) {
         uint32_t s;
         const uint32_t d = quant_quarter(aw[u], sw_quant, &s);
-        a_lds[unit * 64 + lane] = d;
-        if ((lane & 3) == 0) s_lds[(unit >> 2) * 64 + (unit & 3) * 16 + (lane >> 2)] = (uint8_t)s;
+        if constexpr (RB == 8) {
+          // lane t: row t/8, chunk 2*(unit&1) + (t/4)%2, quarter t%4
+          const int blk = unit >> 1;
+          const int ch = 2 * (unit & 1) + ((lane >> 2) & 1);
+          const int r = lane >> 3;
+          a_lds[blk * 256 + ch * 64 + r * 4 + (lane & 3)] = d;
+          if ((lane & 3) == 0) s_lds[blk * 64 + ch * 16 + r] = (uint8_t)s;
+        } else {
+          a_lds[unit * 64 + lane] = d;
+          if ((lane & 3) == 0) s_lds[(unit >> 2) * 64 + (unit & 3) * 16 + (lane >> 2)] = (uint8_t)s;
+        }
       }
     }
-    __syncthreads();
+    if constexpr (WN == 1) {
+      // the blocks this wave reads are the ones it wrote: LDS keeps one
+      // wave's accesses in order, so only the compiler must not reorder
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+      __syncthreads();
+    }
   }
 
   // Phase 3: accumulate.
@@ -241,6 +263,13 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
       } else {
         a = *(const u32x4 *)(a_lds + blk * 256 + lane * 4);
         sa = s_lds[blk * 64 + lane];
+        if constexpr (RB == 8) {
+          // rows 8..15 of the block were not staged: feed zeros
+          if (lane & 8) {
+            a = u32x4{0u, 0u, 0u, 0u};
+            sa = 0u;
+          }
+        }
       }
       const v8i a_op = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
 #pragma unroll
@@ -288,11 +317,33 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
         for (int r = 0; r < 4; ++r) red[wk * E + elem(mt, nt, r)] = acc[mt][nt][r];
     __syncthreads();
     if (split == 1) {
-      for (int e = threadIdx.x; e < E; e += NTH) {
-        float s = 0.f;
+      // eight consecutive elements are eight consecutive columns of one row:
+      // add them over the WK waves and store them as one 16-byte write
+      for (int j = threadIdx.x; j < E / 8; j += NTH) {
+        const int e0 = 8 * j;
+        float v[8];
 #pragma unroll
-        for (int w = 0; w < WK; ++w) s += red[w * E + e];
-        store_c(e, s);
+        for (int q = 0; q < 8; ++q) v[q] = 0.f;
+#pragma unroll
+        for (int w = 0; w < WK; ++w) {
+          const v4f lo = *(const v4f *)(red + w * E + e0);
+          const v4f hi = *(const v4f *)(red + w * E + e0 + 4);
+          v[0] += lo[0]; v[1] += lo[1]; v[2] += lo[2]; v[3] += lo[3];
+          v[4] += hi[0]; v[5] += hi[1]; v[6] += hi[2]; v[7] += hi[3];
+        }
+        const int ln = e0 & 63, i = e0 >> 6;
+        const int r = i & 3, t = i >> 2;
+        const int mt = t / TN, sub = t % TN;
+        const int row = m0 + 16 * mt + 4 * (ln >> 4) + r;
+        const int col = 16 * (n_tile * TN + sub) + (ln & 15);
+        if (row < M) {
+          u32x4 pk;
+          pk.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+          pk.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+          pk.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
+          pk.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
+          *(u32x4 *)(C + (size_t)row * N + col) = pk;
+        }
       }
       return;
     }
@@ -551,7 +602,7 @@ size_t operand_a_bytes(int M, int K) { return (size_t)((M + 15) / 16) * (size_t)
 
 typedef hipError_t (*launch_fn)(const GemmArgs &, int split, bool sw, hipStream_t);
 
-template <int MT, int NT, int WN, int WK, int KPW, bool PREQ>
+template <int MT, int NT, int WN, int WK, int KPW, bool PREQ, int RB>
 static hipError_t launch_variant(const GemmArgs &a, int split, bool sw, hipStream_t stream) {
   const int n_tiles = a.N / (16 * NT * WN);
   const int m_tiles = (a.M + 16 * MT - 1) / (16 * MT);
@@ -569,7 +620,7 @@ static hipError_t launch_variant(const GemmArgs &a, int split, bool sw, hipStrea
   if (split > 1)
     partials = (float *)(ws + kTicketBytes + (PREQ ? ((operand_a_bytes(a.M, a.K) + 255) & ~(size_t)255) : 0));
   dim3 grid((unsigned)(n_tiles * m_tiles * split));
-  gemm_kernel<MT, NT, WN, WK, KPW, PREQ><<<grid, 64 * WN * WK, 0, stream>>>(
+  gemm_kernel<MT, NT, WN, WK, KPW, PREQ, RB><<<grid, 64 * WN * WK, 0, stream>>>(
       (const uint16_t *)a.A, aop, (const uint8_t *)a.Bw, (const uint8_t *)a.Bs, (uint16_t *)a.C, partials, tickets, a.M,
       a.N, a.K, split, n_tiles, sw ? 1 : 0);
   return hipGetLastError();
@@ -598,15 +649,20 @@ static hipError_t launch_loop_variant(const GemmArgs &a, int split, bool sw, hip
 struct Variant {
   int mt, nt, wn, wk, kpw, pq;
   launch_fn fn;
+  int rb;  // rows per staged A block (8: only for M <= 8)
 };
 
-#define V(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 0, launch_variant<MT, NT, WN, WK, KPW, false>}
-#define VQ(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 1, launch_variant<MT, NT, WN, WK, KPW, true>}
+#define V(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 0, launch_variant<MT, NT, WN, WK, KPW, false, 16>, 16}
+#define V8(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 0, launch_variant<MT, NT, WN, WK, KPW, false, 8>, 8}
+#define VQ(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 1, launch_variant<MT, NT, WN, WK, KPW, true, 16>, 16}
 // K-loop kernels (pre-quantized A) are listed with wk = 0 and kpw = the
 // prefetch depth P: they cover any K
-#define VL(MW, NW, WN, P) {MW, NW, WN, 0, P, 1, launch_loop_variant<MW, NW, WN, P>}
+#define VL(MW, NW, WN, P) {MW, NW, WN, 0, P, 1, launch_loop_variant<MW, NW, WN, P>, 16}
 
 static const Variant kVariants[] = {
+    V8(1, 1, 1, 16, 4), V8(1, 1, 1, 14, 4), V8(1, 1, 1, 8, 4), V8(1, 1, 1, 16, 2), V8(1, 1, 2, 8, 4), V8(1, 1, 2, 8, 2),
+    V8(1, 2, 1, 16, 4), V8(1, 2, 1, 8, 4), V8(1, 1, 1, 4, 4), V8(1, 1, 1, 4, 2), V8(1, 1, 1, 8, 2), V8(1, 1, 1, 4, 1),
+    V8(1, 1, 2, 4, 2), V8(1, 1, 4, 4, 4), V8(1, 1, 1, 2, 2), V8(1, 1, 1, 1, 4), V8(1, 1, 1, 2, 4),
     VL(4, 1, 4, 8), VL(4, 1, 4, 16), VL(4, 1, 2, 8), VL(4, 1, 2, 16), VL(4, 2, 4, 8), VL(4, 1, 8, 8),
     VL(4, 1, 8, 16), VL(4, 1, 7, 8), VL(4, 1, 7, 16), VL(8, 1, 4, 8), VL(8, 1, 2, 8), VL(2, 1, 8, 8),
     VL(2, 1, 8, 16), VL(4, 2, 2, 8),
@@ -678,6 +734,7 @@ static const Variant kVariants[] = {
 };
 
 #undef V
+#undef V8
 #undef VQ
 #undef VL
 
@@ -690,13 +747,14 @@ void gemm_variant_shape(int v, Schedule *s) {
   s->wk = kVariants[v].wk;
   s->kpw = kVariants[v].kpw;
   s->pq = kVariants[v].pq;
+  s->rb = kVariants[v].rb;
   s->variant = v;
 }
 
-int find_gemm_variant(int mt, int nt, int wn, int wk, int kpw, int pq) {
+int find_gemm_variant(int mt, int nt, int wn, int wk, int kpw, int pq, int rb) {
   for (int v = 0; v < num_gemm_variants(); ++v)
     if (kVariants[v].mt == mt && kVariants[v].nt == nt && kVariants[v].wn == wn && kVariants[v].wk == wk &&
-        kVariants[v].kpw == kpw && kVariants[v].pq == pq)
+        kVariants[v].kpw == kpw && kVariants[v].pq == pq && kVariants[v].rb == rb)
       return v;
   return -1;
 }

@@ -37,6 +37,7 @@ int tiles_of(const Schedule &s, int M, int N) {
 
 bool covers(const Schedule &s, int M, int N, int K) {
   if (s.split < 1 || N % (16 * s.nt * s.wn) != 0) return false;
+  if (s.rb == 8 && (M > 8 || s.mt != 1)) return false;
   const int ks = (K + 127) / 128;
   if (s.wk > 0 && (ks + s.split - 1) / s.split > s.wk * s.kpw) return false;  // wk == 0: K loop
   if (s.split > 1 && tiles_of(s, M, N) > kMaxSplitTiles) return false;
@@ -53,8 +54,8 @@ struct Tuned {
 };
 const Tuned kTuned[] = {
     {16, 3072, 1536, "mt1_nt1_wn2_wk4_kpw4_split1"},
-    {32, 4096, 512, "mt2_nt1_wn2_wk4_kpw1_split1"},
-    {8, 2112, 7168, "mt1_nt1_wn4_wk4_kpw4_split4"},
+    {32, 4096, 512, "mt2_nt2_wn1_wk4_kpw1_split1"},
+    {8, 2112, 7168, "mt1_nt2_wn1_wk8_kpw4_split2_r8"},
     {64, 7168, 2048, "mt4_nt1_wn2_wk4_kpw4_split1_pq"},
     {256, 7168, 7168, "mt4_nt2_wn4_wk0_kpw8_split1_pq"},
 };
@@ -89,7 +90,7 @@ bool pick_schedule(int M, int N, int K, Schedule *out) {
   for (int v = 0; v < num_gemm_variants(); ++v) {
     Schedule s;
     gemm_variant_shape(v, &s);
-    if (s.mt != mt || s.pq || s.wk == 0) continue;
+    if (s.mt != mt || s.pq || s.wk == 0 || (s.rb == 8) != (M <= 8)) continue;
     for (s.split = 1; s.split <= 16; ++s.split) {
       if (!covers(s, M, N, K)) continue;
       const int per_wg = (ks + s.split - 1) / s.split;
@@ -117,12 +118,16 @@ bool pick_schedule(int M, int N, int K, Schedule *out) {
 bool parse_name(const char *name, Schedule *out) {
   int mt, nt, wn, wk, kpw, split, used = 0;
   if (sscanf(name, "mt%d_nt%d_wn%d_wk%d_kpw%d_split%d%n", &mt, &nt, &wn, &wk, &kpw, &split, &used) != 6) return false;
-  int pq = 0;
-  if (name[used] != 0) {
-    if (strcmp(name + used, "_pq") != 0) return false;
+  int pq = 0, rb = 16;
+  const char *rest = name + used;
+  if (strcmp(rest, "_pq") == 0) {
     pq = 1;
+  } else if (strcmp(rest, "_r8") == 0) {
+    rb = 8;
+  } else if (*rest != 0) {
+    return false;
   }
-  const int v = find_gemm_variant(mt, nt, wn, wk, kpw, pq);
+  const int v = find_gemm_variant(mt, nt, wn, wk, kpw, pq, rb);
   if (v < 0 || split < 1) return false;
   gemm_variant_shape(v, out);
   out->split = split;
@@ -243,7 +248,7 @@ const char *mxfp4_gemm_schedule_name(int64_t M, int64_t N, int64_t K) {
   Schedule s;
   if (!choose((int)M, (int)N, (int)K, &s)) return nullptr;
   snprintf(buf, sizeof(buf), "mt%d_nt%d_wn%d_wk%d_kpw%d_split%d%s", s.mt, s.nt, s.wn, s.wk, s.kpw, s.split,
-           s.pq ? "_pq" : "");
+           s.pq ? "_pq" : (s.rb == 8 ? "_r8" : ""));
   return buf;
 }
 

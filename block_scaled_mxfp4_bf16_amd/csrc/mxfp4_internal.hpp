@@ -17,8 +17,10 @@ namespace mxfp4 {
 //         adds the partial sums from the workspace and stores C
 //   pq    1: A is quantized once by a separate launch into operand blocks in
 //         the workspace and the GEMM reads those; 0: the GEMM quantizes A
+//   rb    rows per staged A block: 16, or 8 (for M <= 8: no loads or
+//         converts are spent on rows that do not exist)
 struct Schedule {
-  int mt, nt, wn, wk, kpw, split, pq;
+  int mt, nt, wn, wk, kpw, split, pq, rb;
   int variant;  // index into the kernel table
 };
 
@@ -41,7 +43,7 @@ struct GemmArgs {
 // Kernel table queries (gemm_kernels.hip).
 int num_gemm_variants();
 void gemm_variant_shape(int v, Schedule *s);  // fills everything but split
-int find_gemm_variant(int mt, int nt, int wn, int wk, int kpw, int pq);
+int find_gemm_variant(int mt, int nt, int wn, int wk, int kpw, int pq, int rb);
 
 size_t gemm_workspace_bytes(const Schedule &s, int M, int N, int K);
 hipError_t launch_gemm(const Schedule &s, const GemmArgs &a, bool sw_quant, hipStream_t stream);

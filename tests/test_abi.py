@@ -118,6 +118,19 @@ def test_schedule_names_and_override():
     assert mx.mxfp4_gemm_schedule_name(16, 3072, 1536) == name
 
 
+def test_eight_row_schedules_only_cover_m_up_to_8():
+    mx.mxfp4_set_schedule_override("mt1_nt1_wn1_wk16_kpw4_split1_r8")
+    try:
+        assert mx.mxfp4_gemm_schedule_name(8, 2112, 7168) == "mt1_nt1_wn1_wk16_kpw4_split1_r8"
+        assert mx.mxfp4_gemm_schedule_name(1, 256, 512) == "mt1_nt1_wn1_wk16_kpw4_split1_r8"
+        assert mx.mxfp4_gemm_schedule_name(9, 2112, 7168) is None
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+    # without an override, small M picks an 8-row schedule unless tuned otherwise
+    assert mx.mxfp4_gemm_schedule_name(4, 512, 1024).endswith("_r8")
+    assert not mx.mxfp4_gemm_schedule_name(9, 512, 1024).endswith("_r8")
+
+
 def test_quant_mode_knob():
     with pytest.raises(RuntimeError):
         mx.mxfp4_set_quant_mode(2)

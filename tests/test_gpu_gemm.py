@@ -208,3 +208,25 @@ def test_k_loop_kernels_ragged(sched):
         mx.mxfp4_set_schedule_override(None)
     assert np.array_equal(got, again)
     assert_close(got, c.ref(), sched)
+
+
+R8_SCHEDULES = ["mt1_nt1_wn1_wk16_kpw4_split1_r8", "mt1_nt1_wn2_wk8_kpw2_split2_r8", "mt1_nt2_wn1_wk8_kpw4_split1_r8",
+                "mt1_nt1_wn1_wk4_kpw1_split5_r8", "mt1_nt1_wn4_wk4_kpw4_split2_r8", "mt1_nt1_wn1_wk1_kpw4_split5_r8"]
+
+
+@pytest.mark.parametrize("sched", R8_SCHEDULES)
+@pytest.mark.parametrize("M", [1, 5, 8])
+def test_eight_row_staging_matches_oracle(sched, M):
+    """A staged in 8-row blocks (rows 8..15 of the matrix operand fed as
+    zeros), with a half step at the end of K and a split that is uneven."""
+    torch = torch_cuda()
+    c = make(torch, M, 256, 2048 + 64, seed=40 + M)
+    mx.mxfp4_set_schedule_override(sched)
+    try:
+        assert mx.mxfp4_gemm_schedule_name(c.M, c.N, c.K) == sched
+        first = c.run()
+        second = c.run()
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+    assert np.array_equal(first, second)
+    assert_close(first, c.ref(), "%s M=%d" % (sched, M))
