@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmxfp4.so")
-SOURCES = ["mxfp4_api.hip", "quant_kernels.hip", "gemm_kernels.hip"]
+SOURCES = ["mxfp4_api.hip", "quant_kernels.hip", "gemm_kernels.hip", "gemm_wide.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -24,6 +24,13 @@ HIPCC_FLAGS = [
     "-fvisibility=hidden",
     "-I" + os.path.join(ROOT, "include"),
 ]
+
+
+# Per-source extra flags.  The scaled matrix instruction has no form whose
+# result is tied to its accumulator input when the accumulator lives in
+# AGPRs, so long accumulation loops get copies between every pair of
+# instructions; keeping accumulators in VGPRs lets them update in place.
+EXTRA_FLAGS = {"gemm_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -42,7 +49,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -42,49 +42,6 @@
 
 namespace mxfp4 {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// Word 3 of a gfx9 buffer resource for raw (untyped) dword access.
-constexpr int kRsrcWord3 = 0x00020000;
-
-// DPP lane patterns within groups of four lanes.
-constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1, 0, 3, 2]
-constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2, 3, 0, 1]
-
-__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadSwap1, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadSwap2, 0xF, 0xF, false));
-  return v;
-}
-
-// Quantize 8 consecutive elements of a 32-element group (4 dwords of bf16
-// pairs) whose other 24 elements sit in the three neighbouring lanes of the
-// same quad: returns the lane's dword of codes and writes the scale byte.
-__device__ __forceinline__ uint32_t quant_quarter(const u32x4 &w, int sw_quant, uint32_t *scale) {
-  u16x2 m = __builtin_bit_cast(u16x2, w.x & 0x7FFF7FFFu);
-  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.y & 0x7FFF7FFFu));
-  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.z & 0x7FFF7FFFu));
-  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.w & 0x7FFF7FFFu));
-  const uint32_t amax = quad_max(m.x > m.y ? m.x : m.y);
-  const uint32_t s = scale_byte_from_amax(amax);
-  *scale = s;
-  uint32_t d = 0;
-  if (!sw_quant) {
-    const float sf = __uint_as_float(s << 23);
-    d = cvt_pair_hw<0>(d, w.x, sf);
-    d = cvt_pair_hw<1>(d, w.y, sf);
-    d = cvt_pair_hw<2>(d, w.z, sf);
-    d = cvt_pair_hw<3>(d, w.w, sf);
-  } else {
-    const float inv = inv_scale_f32(s);
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      d |= (encode_sw(ww[b] & 0xFFFFu, inv) | (encode_sw(ww[b] >> 16, inv) << 4)) << (8 * b);
-  }
-  return d;
-}
-
 template <int MT, int NT, int WN, int WK, int KPW, bool PREQ, int RB>
 __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__restrict__ A,
                                                            const uint8_t *__restrict__ Aop,
@@ -394,10 +351,10 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
 // (m tile, step) holds 1 KiB of codes (operand lane L's 16 bytes at 16*L)
 // and 64 scale bytes.  One wave per 16 rows x 32 elements, four consecutive
 // lanes per group, as in the staging of the fused mode.
-__global__ __launch_bounds__(256) void quant_operand_kernel(const uint16_t *__restrict__ A, uint8_t *__restrict__ Aop,
-                                                            int M, int K, int units, int sw_quant) {
-  const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);  // (m tile, step, chunk), chunk fastest
+__global__ __launch_bounds__(64) void quant_operand_kernel(const uint16_t *__restrict__ A, uint8_t *__restrict__ Aop,
+                                                           int M, int K, int units, int sw_quant) {
+  const int lane = threadIdx.x;
+  const int unit = blockIdx.x;  // (m tile, step, chunk), chunk fastest; one wave per workgroup
   if (unit >= units) return;
   const int KS = (K + 127) >> 7;
   const int ch = unit & 3;
@@ -416,186 +373,6 @@ __global__ __launch_bounds__(256) void quant_operand_kernel(const uint16_t *__re
   if ((lane & 3) == 0) blk[1024 + ch * 16 + (lane >> 2)] = (uint8_t)s;
 }
 
-// Pre-quantized A, long K: a K loop instead of a fully unrolled run.
-// The workgroup owns 16*MW rows x 16*NW*WN columns over the whole K range
-// (or a split of it); its WN waves own NW subtiles each.  Per 128-wide step
-// the workgroup copies the MW operand blocks of A (1088 bytes each) into one
-// of two LDS stages, all waves read them from there, and each wave streams
-// its own B operands from memory, P steps ahead in registers.
-template <int MW, int NW, int WN, int P>
-__global__ __launch_bounds__(64 * WN) void gemm_loop_kernel(const uint8_t *__restrict__ Aop,
-                                                           const uint8_t *__restrict__ Bw,
-                                                           const uint8_t *__restrict__ Bs, uint16_t *__restrict__ C,
-                                                           float *__restrict__ partials,
-                                                           uint32_t *__restrict__ tickets, int M, int N, int K,
-                                                           int split, int n_tiles) {
-  constexpr int NTH = 64 * WN;
-  constexpr int TN = NW * WN;
-  constexpr int E = MW * TN * 256;
-  constexpr int NP = (NW + 1) / 2;
-  constexpr int STAGE = MW * 1088;                  // bytes of A per step
-  constexpr int CHUNKS = STAGE / 16;                // 16-byte pieces per step
-  constexpr int CPT = (CHUNKS + NTH - 1) / NTH;     // pieces per thread
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][STAGE];
-  __shared__ uint32_t s_last;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int bid = blockIdx.x;
-  const int n_tile = bid % n_tiles;
-  const int rest = bid / n_tiles;
-  const int sk = rest % split;
-  const int m_tile = rest / split;
-  const int mb0 = m_tile * MW;  // first 16-row operand block row
-  const int gw = n_tile * TN + wave * NW;
-  const int kc = lane >> 4;
-
-  const int KS = (K + 127) >> 7;
-  const int S0 = (int)((uint32_t)(sk * KS) / (uint32_t)split);
-  const int S1 = (int)((uint32_t)((sk + 1) * KS) / (uint32_t)split);
-  const int gp = ((K >> 5) + 7) & ~7;
-  const int mblocks = (M + 15) >> 4;
-  const int op_bytes = mblocks * KS * 1088;
-  const int b_bytes = (N >> 4) * K * 8;
-  const int s_bytes = ((N + 255) >> 8) * 8 * gp * 32;
-  const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Aop, 0, op_bytes, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Bw, 0, b_bytes, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Bs, 0, s_bytes, kRsrcWord3);
-
-  // A pieces of step ks this thread copies: piece c of block mw sits at
-  // byte 16*c of that block; blocks past M or steps past the run read zeros.
-  auto load_a = [&](int ks, u32x4 (&v)[CPT]) {
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int piece = threadIdx.x + j * NTH;
-      const int mw = piece / 68, c = piece % 68;
-      const int mb = mb0 + mw;
-      const bool ok = piece < CHUNKS && ks < S1 && mb < mblocks;
-      v[j] = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, ok ? (mb * KS + ks) * 1088 + c * 16 : op_bytes, 0, 0);
-    }
-  };
-  auto load_b = [&](int ks, u32x4 (&bv)[NW], uint32_t (&sw)[NP]) {
-    const bool step_ok = ks < S1;
-    const bool ok = step_ok && (ks * 128 + kc * 32 < K);
-#pragma unroll
-    for (int nt = 0; nt < NW; ++nt)
-      bv[nt] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, ok ? (gw + nt) * K * 8 + ks * 1024 + lane * 16 : b_bytes,
-                                                      0, 0);
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int g = gw + 2 * p;
-      sw[p] = __builtin_amdgcn_raw_buffer_load_b32(
-          s_rsrc, step_ok ? (g >> 1) * gp * 32 + (ks >> 1) * 256 + lane * 4 : s_bytes, 0, 0);
-    }
-  };
-
-  v4f acc[MW][NW];
-#pragma unroll
-  for (int mw = 0; mw < MW; ++mw)
-#pragma unroll
-    for (int nt = 0; nt < NW; ++nt) acc[mw][nt] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 av[P][CPT];
-  u32x4 bv[P][NW];
-  uint32_t sw[P][NP];
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    load_a(S0 + p, av[p]);
-    load_b(S0 + p, bv[p], sw[p]);
-  }
-
-  const int iters = (S1 - S0 + P - 1) / P;
-  for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const int ks = S0 + it * P + p;
-      const int buf = p & 1;
-      // stage A of this step
-#pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        const int piece = threadIdx.x + j * NTH;
-        if (CPT * NTH == CHUNKS || piece < CHUNKS) *(u32x4 *)(a_lds[buf] + piece * 16) = av[p][j];
-      }
-      __syncthreads();
-      // refill this slot with the step P ahead
-      load_a(ks + P, av[p]);
-      u32x4 b[NW];
-      uint32_t sc[NP];
-#pragma unroll
-      for (int nt = 0; nt < NW; ++nt) b[nt] = bv[p][nt];
-#pragma unroll
-      for (int q = 0; q < NP; ++q) sc[q] = sw[p][q];
-      load_b(ks + P, bv[p], sw[p]);
-#pragma unroll
-      for (int mw = 0; mw < MW; ++mw) {
-        const u32x4 a = *(const u32x4 *)(a_lds[buf] + mw * 1088 + lane * 16);
-        const uint32_t sa = a_lds[buf][mw * 1088 + 1024 + lane];
-        const v8i a_op = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-#pragma unroll
-        for (int nt = 0; nt < NW; ++nt) {
-          const int g = gw + nt;
-          const uint32_t sel = (uint32_t)((g & 1) | ((ks & 1) << 1));
-          const uint32_t sb = (sc[nt >> 1] >> (8 * sel)) & 0xFFu;
-          const v8i b_op = {(int)b[nt].x, (int)b[nt].y, (int)b[nt].z, (int)b[nt].w, 0, 0, 0, 0};
-          acc[mw][nt] =
-              __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_op, b_op, acc[mw][nt], 4, 4, 0, (int)sa, 0, (int)sb);
-        }
-      }
-    }
-  }
-
-  // Epilogue: accumulator element r of lane l in subtile (mw, nt) is C row
-  // 16*mw + 4*(l/16) + r, column 16*nt + l%16.
-  const int m0 = mb0 * 16;
-  const int tile = m_tile * n_tiles + n_tile;
-  auto col_of = [&](int nt) { return 16 * (gw + nt) + (lane & 15); };
-  if (split == 1) {
-#pragma unroll
-    for (int mw = 0; mw < MW; ++mw)
-#pragma unroll
-      for (int nt = 0; nt < NW; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = m0 + 16 * mw + 4 * (lane >> 4) + r;
-          if (row < M) C[(size_t)row * N + col_of(nt)] = (uint16_t)f32_to_bf16_rne(acc[mw][nt][r]);
-        }
-    return;
-  }
-  // split K across workgroups: slots, ticket, last one adds (as in gemm_kernel)
-  auto elem = [&](int mw, int nt, int r) { return (((mw * WN + wave) * NW + nt) * 4 + r) * 64 + lane; };
-  float *mine = partials + ((size_t)tile * split + sk) * E;
-#pragma unroll
-  for (int mw = 0; mw < MW; ++mw)
-#pragma unroll
-    for (int nt = 0; nt < NW; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        __hip_atomic_store(mine + elem(mw, nt, r), acc[mw][nt][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(&tickets[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                     (uint32_t)(split - 1)
-                 ? 1u
-                 : 0u;
-  __syncthreads();
-  if (!s_last) return;
-  const float *all = partials + (size_t)tile * split * E;
-#pragma unroll
-  for (int mw = 0; mw < MW; ++mw)
-#pragma unroll
-    for (int nt = 0; nt < NW; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = 0.f;
-        for (int j = 0; j < split; ++j)
-          v += __hip_atomic_load(all + (size_t)j * E + elem(mw, nt, r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int row = m0 + 16 * mw + 4 * (lane >> 4) + r;
-        if (row < M) C[(size_t)row * N + col_of(nt)] = (uint16_t)f32_to_bf16_rne(v);
-      }
-  if (threadIdx.x == 0) __hip_atomic_store(&tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 size_t operand_a_bytes(int M, int K) { return (size_t)((M + 15) / 16) * (size_t)((K + 127) / 128) * 1088; }
 
 // ---------------------------------------------------------------- table
@@ -611,14 +388,14 @@ static hipError_t launch_variant(const GemmArgs &a, int split, bool sw, hipStrea
   if (PREQ) {
     aop = (uint8_t *)(ws + kTicketBytes);
     const int units = ((a.M + 15) / 16) * ((a.K + 127) / 128) * 4;
-    quant_operand_kernel<<<(units + 3) / 4, 256, 0, stream>>>((const uint16_t *)a.A, aop, a.M, a.K, units, sw ? 1 : 0);
+    quant_operand_kernel<<<units, 64, 0, stream>>>((const uint16_t *)a.A, aop, a.M, a.K, units, sw ? 1 : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   uint32_t *tickets = (uint32_t *)ws;
   float *partials = nullptr;
   if (split > 1)
-    partials = (float *)(ws + kTicketBytes + (PREQ ? ((operand_a_bytes(a.M, a.K) + 255) & ~(size_t)255) : 0));
+    partials = (float *)(ws + kTicketBytes + (PREQ ? ((pq_operand_bytes(a.M, a.K) + 255) & ~(size_t)255) : 0));
   dim3 grid((unsigned)(n_tiles * m_tiles * split));
   gemm_kernel<MT, NT, WN, WK, KPW, PREQ, RB><<<grid, 64 * WN * WK, 0, stream>>>(
       (const uint16_t *)a.A, aop, (const uint8_t *)a.Bw, (const uint8_t *)a.Bs, (uint16_t *)a.C, partials, tickets, a.M,
@@ -626,61 +403,25 @@ static hipError_t launch_variant(const GemmArgs &a, int split, bool sw, hipStrea
   return hipGetLastError();
 }
 
-template <int MW, int NW, int WN, int P>
-static hipError_t launch_loop_variant(const GemmArgs &a, int split, bool sw, hipStream_t stream) {
-  const int n_tiles = a.N / (16 * NW * WN);
-  const int m_tiles = (a.M + 16 * MW - 1) / (16 * MW);
-  char *ws = (char *)a.workspace;
-  uint8_t *aop = (uint8_t *)(ws + kTicketBytes);
-  const int units = ((a.M + 15) / 16) * ((a.K + 127) / 128) * 4;
-  quant_operand_kernel<<<(units + 3) / 4, 256, 0, stream>>>((const uint16_t *)a.A, aop, a.M, a.K, units, sw ? 1 : 0);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  uint32_t *tickets = (uint32_t *)ws;
-  float *partials =
-      split > 1 ? (float *)(ws + kTicketBytes + ((operand_a_bytes(a.M, a.K) + 255) & ~(size_t)255)) : nullptr;
-  dim3 grid((unsigned)(n_tiles * m_tiles * split));
-  gemm_loop_kernel<MW, NW, WN, P><<<grid, 64 * WN, 0, stream>>>(aop, (const uint8_t *)a.Bw, (const uint8_t *)a.Bs,
-                                                                 (uint16_t *)a.C, partials, tickets, a.M, a.N, a.K,
-                                                                 split, n_tiles);
-  return hipGetLastError();
-}
-
 struct Variant {
   int mt, nt, wn, wk, kpw, pq;
   launch_fn fn;
-  int rb;  // rows per staged A block (8: only for M <= 8)
+  int rb;    // rows per staged A block (8: only for M <= 8)
+  int wide;  // the large-M kernel of gemm_wide.hip
 };
 
-#define V(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 0, launch_variant<MT, NT, WN, WK, KPW, false, 16>, 16}
-#define V8(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 0, launch_variant<MT, NT, WN, WK, KPW, false, 8>, 8}
-#define VQ(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 1, launch_variant<MT, NT, WN, WK, KPW, true, 16>, 16}
-// K-loop kernels (pre-quantized A) are listed with wk = 0 and kpw = the
-// prefetch depth P: they cover any K
-#define VL(MW, NW, WN, P) {MW, NW, WN, 0, P, 1, launch_loop_variant<MW, NW, WN, P>, 16}
+#define V(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 0, launch_variant<MT, NT, WN, WK, KPW, false, 16>, 16, 0}
+#define V8(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 0, launch_variant<MT, NT, WN, WK, KPW, false, 8>, 8, 0}
+#define VQ(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 1, launch_variant<MT, NT, WN, WK, KPW, true, 16>, 16, 0}
+// large-M kernels: W waves split K; listed with wn = 1, wk = W, kpw = the
+// number of steps loaded ahead
+#define VW(MW, NW, W, D) {MW, NW, 1, W, D, 1, launch_wide_##MW##_##NW##_##W##_##D, 16, 1},
 
 static const Variant kVariants[] = {
+    MXFP4_WIDE_VARIANTS(VW)
     V8(1, 1, 1, 16, 4), V8(1, 1, 1, 14, 4), V8(1, 1, 1, 8, 4), V8(1, 1, 1, 16, 2), V8(1, 1, 2, 8, 4), V8(1, 1, 2, 8, 2),
     V8(1, 2, 1, 16, 4), V8(1, 2, 1, 8, 4), V8(1, 1, 1, 4, 4), V8(1, 1, 1, 4, 2), V8(1, 1, 1, 8, 2), V8(1, 1, 1, 4, 1),
     V8(1, 1, 2, 4, 2), V8(1, 1, 4, 4, 4), V8(1, 1, 1, 2, 2), V8(1, 1, 1, 1, 4), V8(1, 1, 1, 2, 4),
-    VL(4, 1, 4, 8), VL(4, 1, 4, 16), VL(4, 1, 2, 8), VL(4, 1, 2, 16), VL(4, 2, 4, 8), VL(4, 1, 8, 8),
-    VL(4, 1, 8, 16), VL(4, 1, 7, 8), VL(4, 1, 7, 16), VL(8, 1, 4, 8), VL(8, 1, 2, 8), VL(2, 1, 8, 8),
-    VL(2, 1, 8, 16), VL(4, 2, 2, 8),
-    VL(2, 1, 1, 2), VL(2, 1, 1, 4), VL(2, 1, 2, 2), VL(2, 1, 2, 4), VL(2, 1, 4, 2), VL(2, 1, 4, 4),
-    VL(2, 1, 7, 2), VL(2, 1, 7, 4), VL(2, 1, 8, 2), VL(2, 1, 8, 4), VL(2, 2, 1, 2), VL(2, 2, 1, 4),
-    VL(2, 2, 2, 2), VL(2, 2, 2, 4), VL(2, 2, 4, 2), VL(2, 2, 4, 4), VL(2, 2, 7, 2), VL(2, 2, 7, 4),
-    VL(2, 2, 8, 2), VL(2, 2, 8, 4), VL(2, 4, 1, 2), VL(2, 4, 1, 4), VL(2, 4, 2, 2), VL(2, 4, 2, 4),
-    VL(2, 4, 4, 2), VL(2, 4, 4, 4), VL(2, 4, 7, 2), VL(2, 4, 7, 4), VL(2, 4, 8, 2), VL(2, 4, 8, 4),
-    VL(4, 1, 1, 2), VL(4, 1, 1, 4), VL(4, 1, 2, 2), VL(4, 1, 2, 4), VL(4, 1, 4, 2), VL(4, 1, 4, 4),
-    VL(4, 1, 7, 2), VL(4, 1, 7, 4), VL(4, 1, 8, 2), VL(4, 1, 8, 4), VL(4, 2, 1, 2), VL(4, 2, 1, 4),
-    VL(4, 2, 2, 2), VL(4, 2, 2, 4), VL(4, 2, 4, 2), VL(4, 2, 4, 4), VL(4, 2, 7, 2), VL(4, 2, 7, 4),
-    VL(4, 2, 8, 2), VL(4, 2, 8, 4), VL(4, 4, 1, 2), VL(4, 4, 1, 4), VL(4, 4, 2, 2), VL(4, 4, 2, 4),
-    VL(4, 4, 4, 2), VL(4, 4, 4, 4), VL(4, 4, 7, 2), VL(4, 4, 7, 4), VL(4, 4, 8, 2), VL(4, 4, 8, 4),
-    VL(8, 1, 1, 2), VL(8, 1, 1, 4), VL(8, 1, 2, 2), VL(8, 1, 2, 4), VL(8, 1, 4, 2), VL(8, 1, 4, 4),
-    VL(8, 1, 7, 2), VL(8, 1, 7, 4), VL(8, 1, 8, 2), VL(8, 1, 8, 4), VL(8, 2, 1, 2), VL(8, 2, 1, 4),
-    VL(8, 2, 2, 2), VL(8, 2, 2, 4), VL(8, 2, 4, 2), VL(8, 2, 4, 4), VL(8, 2, 7, 2), VL(8, 2, 7, 4),
-    VL(8, 2, 8, 2), VL(8, 2, 8, 4), VL(8, 4, 1, 2), VL(8, 4, 2, 2), VL(8, 4, 4, 2), VL(8, 4, 7, 2),
-    VL(8, 4, 8, 2),
     V(1, 1, 1, 1, 1), V(1, 1, 1, 1, 2), V(1, 1, 1, 1, 4), V(1, 1, 1, 2, 1), V(1, 1, 1, 2, 2), V(1, 1, 1, 2, 4),
     V(1, 1, 1, 4, 1), V(1, 1, 1, 4, 2), V(1, 1, 1, 4, 4), V(1, 1, 1, 8, 1), V(1, 1, 1, 8, 2), V(1, 1, 1, 8, 4),
     V(1, 1, 1, 16, 1), V(1, 1, 1, 16, 2), V(1, 1, 2, 1, 1), V(1, 1, 2, 1, 2), V(1, 1, 2, 1, 4), V(1, 1, 2, 2, 1),
@@ -734,9 +475,9 @@ static const Variant kVariants[] = {
 };
 
 #undef V
+#undef VW
 #undef V8
 #undef VQ
-#undef VL
 
 int num_gemm_variants() { return (int)(sizeof(kVariants) / sizeof(kVariants[0])); }
 
@@ -748,13 +489,14 @@ void gemm_variant_shape(int v, Schedule *s) {
   s->kpw = kVariants[v].kpw;
   s->pq = kVariants[v].pq;
   s->rb = kVariants[v].rb;
+  s->wide = kVariants[v].wide;
   s->variant = v;
 }
 
-int find_gemm_variant(int mt, int nt, int wn, int wk, int kpw, int pq, int rb) {
+int find_gemm_variant(int mt, int nt, int wn, int wk, int kpw, int pq, int rb, int wide) {
   for (int v = 0; v < num_gemm_variants(); ++v)
     if (kVariants[v].mt == mt && kVariants[v].nt == nt && kVariants[v].wn == wn && kVariants[v].wk == wk &&
-        kVariants[v].kpw == kpw && kVariants[v].pq == pq && kVariants[v].rb == rb)
+        kVariants[v].kpw == kpw && kVariants[v].pq == pq && kVariants[v].rb == rb && kVariants[v].wide == wide)
       return v;
   return -1;
 }
@@ -762,7 +504,7 @@ int find_gemm_variant(int mt, int nt, int wn, int wk, int kpw, int pq, int rb) {
 size_t gemm_workspace_bytes(const Schedule &s, int M, int N, int K) {
   if (s.split <= 1 && !s.pq) return 0;
   size_t bytes = kTicketBytes;
-  if (s.pq) bytes += (operand_a_bytes(M, K) + 255) & ~(size_t)255;
+  if (s.pq) bytes += (pq_operand_bytes(M, K) + 255) & ~(size_t)255;
   if (s.split > 1) {
     const size_t tiles = (size_t)(N / (16 * s.nt * s.wn)) * (size_t)((M + 16 * s.mt - 1) / (16 * s.mt));
     const size_t e = (size_t)s.mt * s.nt * s.wn * 256;

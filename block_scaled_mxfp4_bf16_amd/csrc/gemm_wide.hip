@@ -1,0 +1,389 @@
+// Large-M MXFP4 GEMM for gfx950: A quantized once by its own launch, then a
+// K loop in which the waves of a workgroup split K instead of the tile.
+//
+// Submission 711914 quantizes A with a standalone kernel when M is large
+// and hands the FP4 operands to a GEMM; this is that split, with our own
+// kernels.  The design follows from what bounds the shape on MI355X:
+//   - Each CU can take in about 64 bytes per clock through its load path.
+//     A workgroup that owns a BM x BN output tile reads (BM + BN) * K / 2
+//     bytes of codes, so the tile should be as close to square as the grid
+//     allows: at 256 x 7168 x 7168, 64 x 112 tiles make exactly 256
+//     workgroups, one per CU.
+//   - Every wave holds the accumulators of the whole tile and takes every
+//     fourth 128-wide K step, loading that step's operands straight into
+//     registers three steps ahead.  No byte is loaded twice by one
+//     workgroup and nothing passes through LDS in the loop; the four
+//     partial tiles are added through LDS once, at the end.
+//   - Workgroups that share B columns run on one XCD (workgroups are
+//     dealt to the eight XCDs in turn), so B comes from HBM about once and
+//     from that XCD's L2 for the other row tiles.
+//
+// Quad-packed operand layout of quantized A (the workspace holds it):
+//   codes   for 16-row tile t < 4*MQ and K step ks < KS (MQ = ceil(M/64),
+//           KS = ceil(K/128)): 1 KiB at (t*KS + ks)*1024, operand lane L's
+//           16 bytes at 16*L -- rows 16t + L%16, K chunk L/16 of the step,
+//           32 codes with element 2i in the low nibble of byte i;
+//   scales  after the codes, for tile quad q and step ks: 256 bytes at
+//           (q*KS + ks)*256; dword L holds operand lane L's scale bytes of
+//           tiles 4q..4q+3 (byte j for tile 4q+j).
+// One dword per lane then serves the scale operand of four matrix
+// instructions, selected by the instruction's operand byte select.
+#include "mxfp4_device.hpp"
+#include "mxfp4_internal.hpp"
+
+namespace mxfp4 {
+
+size_t quad_operand_bytes(int M, int K) {
+  const size_t mq = (size_t)((M + 63) / 64), ks = (size_t)((K + 127) / 128);
+  return mq * ks * (4 * 1024 + 256);
+}
+
+// One single-wave workgroup per (tile quad, K step): 64 rows x 128
+// elements of bf16 A, in sixteen coalesced 16-byte loads per lane (each
+// covers 16 rows x one 32-element group, four lanes per group, as in the
+// fused kernels' staging).  One wave per workgroup spreads the units over
+// as many CUs as there are units: each CU's intake from HBM, not the
+// arithmetic, is what bounds this kernel.  Rows past M and chunks past K
+// load as zeros and are written as zero codes with scale byte 0.
+__global__ __launch_bounds__(64) void quant_quad_kernel(const uint16_t *__restrict__ A, uint8_t *__restrict__ Aop,
+                                                        int M, int K, int units, int sw_quant) {
+  const int lane = threadIdx.x;
+  const int unit = blockIdx.x;
+  if (unit >= units) return;
+  const int KS = (K + 127) >> 7;
+  const int ks = unit % KS;
+  const int q = unit / KS;
+  const int mq = (M + 63) >> 6;
+  const int a_bytes = M * K * 2;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, a_bytes, kRsrcWord3);
+  u32x4 w[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      const int row = (4 * q + j) * 16 + (lane >> 2);
+      const int kel = ks * 128 + ch * 32 + (lane & 3) * 8;
+      const bool ok = (row < M) && (ks * 128 + ch * 32 < K);
+      w[j][ch] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ok ? (row * K + kel) * 2 : a_bytes, 0, 0);
+    }
+  uint32_t *codes = (uint32_t *)Aop;
+  uint32_t *scales = (uint32_t *)(Aop + (size_t)mq * 4 * KS * 1024);
+  uint32_t sc[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      uint32_t s;
+      const uint32_t d = quant_quarter(w[j][ch], sw_quant, &s);
+      // lane = 4*row + quarter: dword (16*ch + row)*4 + quarter of the block
+      codes[(size_t)((4 * q + j) * KS + ks) * 256 + ch * 64 + lane] = d;
+      sc[ch] |= s << (8 * j);
+    }
+  if ((lane & 3) == 0) {
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) scales[(size_t)(q * KS + ks) * 64 + ch * 16 + (lane >> 2)] = sc[ch];
+  }
+}
+
+// Scaled FP4 x FP4 matrix instruction whose A scale is byte `sel` of the
+// scale dword (the instruction's byte select must be a constant; `sel` is
+// one after unrolling).
+__device__ __forceinline__ v4f mfma_fp4_sel(const v8i &a, const v8i &b, const v4f &c, int sel, uint32_t sa,
+                                            uint32_t sb) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, (int)sa, 0, (int)sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 1, (int)sa, 0, (int)sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 2, (int)sa, 0, (int)sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 3, (int)sa, 0, (int)sb);
+  }
+}
+
+// Uniform part of a buffer offset, moved out of range (bit 31) unless
+// `in_range`; the lane's part is added to it afterwards (all offsets stay
+// below 2^31, so the sum is out of range exactly when the flag is set).
+__device__ __forceinline__ int uniform_off(bool in_range, int off) {
+  return off | (in_range ? 0 : (int)0x80000000u);
+}
+
+// Workgroup: W waves (two per SIMD when W = 8), output tile of 16*MW rows x
+// 16*NW columns, K steps [S0, S1) of its split; wave w takes steps S0 + w,
+// S0 + w + W, ...  Each wave keeps the whole tile's accumulators in
+// registers and D steps of operands in flight.
+template <int MW, int NW, int W, int D>
+__global__ __launch_bounds__(64 * W) void gemm_wide_kernel(const uint8_t *__restrict__ Aop,
+                                                          const uint8_t *__restrict__ Bw,
+                                                          const uint8_t *__restrict__ Bs, uint16_t *__restrict__ C,
+                                                          float *__restrict__ partials,
+                                                          uint32_t *__restrict__ tickets, int M, int N, int K,
+                                                          int split, int n_tiles, int m_tiles) {
+  static_assert(MW % 4 == 0, "A scales come as one dword per four row tiles");
+  static_assert(W == 4 || W == 8, "four or eight waves");
+  constexpr int NTH = 64 * W;
+  constexpr int MQ = MW / 4;
+  constexpr int NSD = (NW + 1) / 2;  // B scale dwords per step: 32-row blocks the NW subtiles touch
+  constexpr int E = MW * NW * 256;   // outputs per tile
+  constexpr int RS = 4;              // partial tiles LDS holds at once
+  static_assert(RS * E * 4 <= 160 * 1024 - 64, "partial tiles must fit in LDS");
+  __shared__ __attribute__((aligned(16))) float red[RS * E];
+  __shared__ uint32_t s_last;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // Workgroup b runs on XCD b % 8.  Give each XCD a contiguous range of
+  // (n tile, m tile, split) indices, split and m tile fastest, so that the
+  // workgroups reading the same B columns share one L2.
+  const int G = gridDim.x;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int g8 = G >> 3, r8 = G & 7;
+  const int lin = xcd < r8 ? xcd * (g8 + 1) + slot : r8 * (g8 + 1) + (xcd - r8) * g8 + slot;
+  const int sk = lin % split;
+  const int mn = lin / split;
+  const int m_tile = mn % m_tiles;
+  const int n_tile = mn / m_tiles;
+  const int gw = n_tile * NW;  // first 16-row group of B
+  const int t0 = m_tile * MW;  // first 16-row tile of A
+
+  const int KS = (K + 127) >> 7;
+  const int S0 = (int)((uint32_t)(sk * KS) / (uint32_t)split);
+  const int S1 = (int)((uint32_t)((sk + 1) * KS) / (uint32_t)split);
+  const int gp = ((K >> 5) + 7) & ~7;
+  const int kc = lane >> 4;
+
+  // Out-of-range offsets read zeros: tiles past the quantized rows, steps
+  // past the run, and the missing half of a final 64-wide step.
+  const int mq_all = (M + 63) >> 6;
+  const int codes_bytes = mq_all * 4 * KS * 1024;
+  const int ascale_bytes = mq_all * KS * 256;
+  const int b_bytes = (N >> 4) * K * 8;
+  const int s_bytes = ((N + 255) >> 8) * 8 * gp * 32;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Aop, 0, codes_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t as_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(Aop + codes_bytes), 0, ascale_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Bw, 0, b_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Bs, 0, s_bytes, kRsrcWord3);
+  // the lane's byte in a 1 KiB operand block and in a 256-byte scale block;
+  // a final half step leaves K chunks 2 and 3 of B out of range
+  const int l16 = lane * 16, l4 = lane * 4;
+  const int half_k = (K & 127) != 0;
+  const int l16b = (half_k && kc >= 2) ? (int)0x80000000u : l16;
+
+  struct Stage {
+    u32x4 a[MW];
+    uint32_t as[MQ];
+    u32x4 b[NW];
+    uint32_t bs[NSD];
+  };
+  auto load = [&](int ks, Stage &st) {
+    const bool ok = ks < S1;
+    const int lb = ks == KS - 1 ? l16b : l16;
+#pragma unroll
+    for (int mw = 0; mw < MW; ++mw)
+      st.a[mw] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, uniform_off(ok, ((t0 + mw) * KS + ks) * 1024) + l16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < MQ; ++q)
+      st.as[q] = __builtin_amdgcn_raw_buffer_load_b32(
+          as_rsrc, uniform_off(ok, ((m_tile * MQ + q) * KS + ks) * 256) + l4, 0, 0);
+#pragma unroll
+    for (int nt = 0; nt < NW; ++nt)
+      st.b[nt] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, uniform_off(ok, (gw + nt) * K * 8 + ks * 1024) + lb, 0, 0);
+#pragma unroll
+    for (int d = 0; d < NSD; ++d)
+      st.bs[d] = __builtin_amdgcn_raw_buffer_load_b32(
+          s_rsrc, uniform_off(ok, ((gw >> 1) + d) * gp * 32 + (ks >> 1) * 256) + l4, 0, 0);
+  };
+
+  // The scale byte of B subtile nt: the dword of its 32-row block, byte
+  // (row block half) | 2 * (step parity); a wave's steps all share a parity
+  // when W is even.
+  const int ks0 = S0 + wave;
+  const int odd = gw & 1;
+  uint32_t bshift[NW];
+#pragma unroll
+  for (int nt = 0; nt < NW; ++nt) bshift[nt] = 8u * (uint32_t)(((gw + nt) & 1) | ((ks0 & 1) << 1));
+
+  v4f acc[MW][NW];
+#pragma unroll
+  for (int mw = 0; mw < MW; ++mw)
+#pragma unroll
+    for (int nt = 0; nt < NW; ++nt) acc[mw][nt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Stage &st) {
+    uint32_t sb[NW];
+#pragma unroll
+    for (int nt = 0; nt < NW; ++nt) {
+      const uint32_t dw = (NW % 2 == 0) ? st.bs[nt >> 1] : (odd ? st.bs[(nt + 1) >> 1] : st.bs[nt >> 1]);
+      sb[nt] = (dw >> bshift[nt]) & 0xFFu;
+    }
+#pragma unroll
+    for (int mw = 0; mw < MW; ++mw) {
+      const v8i a_op = {(int)st.a[mw].x, (int)st.a[mw].y, (int)st.a[mw].z, (int)st.a[mw].w, 0, 0, 0, 0};
+#pragma unroll
+      for (int nt = 0; nt < NW; ++nt) {
+        const v8i b_op = {(int)st.b[nt].x, (int)st.b[nt].y, (int)st.b[nt].z, (int)st.b[nt].w, 0, 0, 0, 0};
+        acc[mw][nt] = mfma_fp4_sel(a_op, b_op, acc[mw][nt], mw & 3, st.as[mw >> 2], sb[nt]);
+      }
+    }
+  };
+
+  // The load counter retires in issue order, so a stage's data has arrived
+  // once no more than D - 1 stages' loads are outstanding, provided the
+  // loads go out stage by stage: scheduling barriers keep the compiler from
+  // interleaving them.  The loop has no branch inside (a branch that skips
+  // a load or a use makes the compiler wait for every load in flight where
+  // the paths meet); steps past the run load zeros and add nothing, and the
+  // last round issues no loads.
+  Stage st[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    load(ks0 + W * d, st[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int nsteps = ks0 < S1 ? (S1 - ks0 + W - 1) / W : 0;
+  const int rounds = (nsteps + D - 1) / D;
+  for (int it = 0; it + 1 < rounds; ++it) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      compute(st[d]);
+      __builtin_amdgcn_sched_barrier(0);
+      load(ks0 + W * ((it + 1) * D + d), st[d]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (rounds > 0) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) compute(st[d]);
+  }
+
+  // Add the waves' tiles through LDS, four at a time.  Element index e =
+  // ((mw*NW + nt)*4 + r)*64 + l is accumulator element r of lane l in
+  // subtile (mw, nt): C row 16*mw + 4*(l/16) + r, column 16*nt + l%16, so
+  // eight consecutive e are eight consecutive columns of one row.  With
+  // eight waves, waves 4..7 hand their tiles to waves 0..3 first.
+  auto put = [&](int slot) {
+#pragma unroll
+    for (int mw = 0; mw < MW; ++mw)
+#pragma unroll
+      for (int nt = 0; nt < NW; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[slot * E + ((mw * NW + nt) * 4 + r) * 64 + lane] = acc[mw][nt][r];
+  };
+  if constexpr (W == 8) {
+    if (wave >= 4) put(wave - 4);
+    __syncthreads();
+    if (wave < 4) {
+#pragma unroll
+      for (int mw = 0; mw < MW; ++mw)
+#pragma unroll
+        for (int nt = 0; nt < NW; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[mw][nt][r] += red[wave * E + ((mw * NW + nt) * 4 + r) * 64 + lane];
+    }
+    __syncthreads();
+    if (wave < 4) put(wave);
+  } else {
+    put(wave);
+  }
+  __syncthreads();
+
+  const int m0 = t0 * 16;
+  auto sum8 = [&](int e0, float (&v)[8]) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = 0.f;
+#pragma unroll
+    for (int w = 0; w < RS; ++w) {
+      const v4f lo = *(const v4f *)(red + w * E + e0);
+      const v4f hi = *(const v4f *)(red + w * E + e0 + 4);
+      v[0] += lo[0]; v[1] += lo[1]; v[2] += lo[2]; v[3] += lo[3];
+      v[4] += hi[0]; v[5] += hi[1]; v[6] += hi[2]; v[7] += hi[3];
+    }
+  };
+  auto store8 = [&](int e0, const float (&v)[8]) {
+    const int ln = e0 & 63, i = e0 >> 6;
+    const int r = i & 3, t = i >> 2;
+    const int mw = t / NW, nt = t % NW;
+    const int row = m0 + 16 * mw + 4 * (ln >> 4) + r;
+    const int col = 16 * (gw + nt) + (ln & 15);
+    if (row < M) {
+      u32x4 pk;
+      pk.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+      pk.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+      pk.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
+      pk.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
+      *(u32x4 *)(C + (size_t)row * N + col) = pk;
+    }
+  };
+
+  if (split == 1) {
+    for (int j = threadIdx.x; j < E / 8; j += NTH) {
+      float v[8];
+      sum8(8 * j, v);
+      store8(8 * j, v);
+    }
+    return;
+  }
+
+  // Split K across workgroups: the same slot-and-ticket protocol as the
+  // fused kernels (device-coherent slot stores, wait, ticket; the last
+  // workgroup adds the slots in split order and resets the ticket).
+  const int tile = m_tile * n_tiles + n_tile;
+  float *mine = partials + ((size_t)tile * split + sk) * E;
+  for (int j = threadIdx.x; j < E / 8; j += NTH) {
+    float v[8];
+    sum8(8 * j, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      __hip_atomic_store(mine + 8 * j + q, v[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(&tickets[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     (uint32_t)(split - 1)
+                 ? 1u
+                 : 0u;
+  __syncthreads();
+  if (!s_last) return;
+  const float *all = partials + (size_t)tile * split * E;
+  for (int j = threadIdx.x; j < E / 8; j += NTH) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = 0.f;
+    for (int s = 0; s < split; ++s)
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        v[q] += __hip_atomic_load(all + (size_t)s * E + 8 * j + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    store8(8 * j, v);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int MW, int NW, int W, int D>
+static hipError_t launch_wide(const GemmArgs &a, int split, bool sw, hipStream_t stream) {
+  char *ws = (char *)a.workspace;
+  uint8_t *aop = (uint8_t *)(ws + kTicketBytes);
+  const int units = ((a.M + 63) / 64) * ((a.K + 127) / 128);
+  quant_quad_kernel<<<units, 64, 0, stream>>>((const uint16_t *)a.A, aop, a.M, a.K, units, sw ? 1 : 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_tiles = a.N / (16 * NW);
+  const int m_tiles = (a.M + 16 * MW - 1) / (16 * MW);
+  uint32_t *tickets = (uint32_t *)ws;
+  float *partials =
+      split > 1 ? (float *)(ws + kTicketBytes + ((pq_operand_bytes(a.M, a.K) + 255) & ~(size_t)255)) : nullptr;
+  dim3 grid((unsigned)(n_tiles * m_tiles * split));
+  gemm_wide_kernel<MW, NW, W, D><<<grid, 64 * W, 0, stream>>>(aop, (const uint8_t *)a.Bw, (const uint8_t *)a.Bs,
+                                                               (uint16_t *)a.C, partials, tickets, a.M, a.N, a.K,
+                                                               split, n_tiles, m_tiles);
+  return hipGetLastError();
+}
+
+#define MXFP4_DEFINE_WIDE(MW, NW, W, D)                                                                          \
+  hipError_t launch_wide_##MW##_##NW##_##W##_##D(const GemmArgs &a, int split, bool sw, hipStream_t stream) { \
+    return launch_wide<MW, NW, W, D>(a, split, sw, stream);                                                     \
+  }
+MXFP4_WIDE_VARIANTS(MXFP4_DEFINE_WIDE)
+#undef MXFP4_DEFINE_WIDE
+
+}  // namespace mxfp4

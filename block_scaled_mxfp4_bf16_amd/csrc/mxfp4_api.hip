@@ -39,7 +39,8 @@ bool covers(const Schedule &s, int M, int N, int K) {
   if (s.split < 1 || N % (16 * s.nt * s.wn) != 0) return false;
   if (s.rb == 8 && (M > 8 || s.mt != 1)) return false;
   const int ks = (K + 127) / 128;
-  if (s.wk > 0 && (ks + s.split - 1) / s.split > s.wk * s.kpw) return false;  // wk == 0: K loop
+  // the wide kernel loops over K; the others cover wk * kpw steps per split
+  if (!s.wide && (ks + s.split - 1) / s.split > s.wk * s.kpw) return false;
   if (s.split > 1 && tiles_of(s, M, N) > kMaxSplitTiles) return false;
   return true;
 }
@@ -57,7 +58,7 @@ const Tuned kTuned[] = {
     {32, 4096, 512, "mt2_nt2_wn1_wk4_kpw1_split1"},
     {8, 2112, 7168, "mt1_nt2_wn1_wk8_kpw4_split2_r8"},
     {64, 7168, 2048, "mt4_nt1_wn2_wk4_kpw4_split1_pq"},
-    {256, 7168, 7168, "mt4_nt2_wn4_wk0_kpw8_split1_pq"},
+    {256, 7168, 7168, "wide_mt4_nt7_w4_d2_split1"},
 };
 
 bool pick_schedule(int M, int N, int K, Schedule *out) {
@@ -70,16 +71,36 @@ bool pick_schedule(int M, int N, int K, Schedule *out) {
       }
     }
   if (M > 64) {
-    // large M: A quantized once, a K loop over 64-row x 128-column tiles
-    // (narrower when N does not divide)
-    static const char *const kLarge[] = {"mt4_nt2_wn4_wk0_kpw8_split1_pq", "mt4_nt1_wn4_wk0_kpw8_split1_pq",
-                                         "mt4_nt1_wn2_wk0_kpw8_split1_pq"};
-    for (const char *n : kLarge) {
+    // large M: the wide kernel whose workgroups take in the fewest bytes
+    // each.  Per workgroup, a K step brings 1088 bytes of A per row tile and
+    // about 1152 of B per column subtile; a split adds its partial tiles;
+    // more workgroups than CUs run in rounds.
+    const int ks = (K + 127) / 128;
+    bool found = false;
+    Schedule best{};
+    double best_cost = 0;
+    for (int v = 0; v < num_gemm_variants(); ++v) {
       Schedule s;
-      if (parse_name(n, &s) && covers(s, M, N, K)) {
-        *out = s;
-        return true;
+      gemm_variant_shape(v, &s);
+      if (!s.wide) continue;
+      for (s.split = 1; s.split <= 8; ++s.split) {
+        if (!covers(s, M, N, K)) continue;
+        const int wgs = tiles_of(s, M, N) * s.split;
+        const double rounds = (double)((wgs + 255) / 256);
+        const double steps = (double)((ks + s.split - 1) / s.split);
+        double cost = rounds * (steps * (1.0625 * s.mt + 1.125 * s.nt) + 8.0);
+        if (s.split > 1) cost += 0.5 * s.mt * s.nt * s.split;
+        cost += 0.01 * (8 - s.wk) + 0.001 * (4 - s.kpw);  // more waves, then deeper prefetch, on a tie
+        if (!found || cost < best_cost) {
+          found = true;
+          best_cost = cost;
+          best = s;
+        }
       }
+    }
+    if (found) {
+      *out = best;
+      return true;
     }
   }
   const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
@@ -90,7 +111,7 @@ bool pick_schedule(int M, int N, int K, Schedule *out) {
   for (int v = 0; v < num_gemm_variants(); ++v) {
     Schedule s;
     gemm_variant_shape(v, &s);
-    if (s.mt != mt || s.pq || s.wk == 0 || (s.rb == 8) != (M <= 8)) continue;
+    if (s.mt != mt || s.pq || s.wide || (s.rb == 8) != (M <= 8)) continue;
     for (s.split = 1; s.split <= 16; ++s.split) {
       if (!covers(s, M, N, K)) continue;
       const int per_wg = (ks + s.split - 1) / s.split;
@@ -117,17 +138,26 @@ bool pick_schedule(int M, int N, int K, Schedule *out) {
 // "mt1_nt1_wn2_wk4_kpw1_split2", with "_pq" appended for the pre-quantized mode
 bool parse_name(const char *name, Schedule *out) {
   int mt, nt, wn, wk, kpw, split, used = 0;
-  if (sscanf(name, "mt%d_nt%d_wn%d_wk%d_kpw%d_split%d%n", &mt, &nt, &wn, &wk, &kpw, &split, &used) != 6) return false;
-  int pq = 0, rb = 16;
-  const char *rest = name + used;
-  if (strcmp(rest, "_pq") == 0) {
-    pq = 1;
-  } else if (strcmp(rest, "_r8") == 0) {
-    rb = 8;
-  } else if (*rest != 0) {
-    return false;
+  int v;
+  if (strncmp(name, "wide_", 5) == 0) {
+    int w, d;
+    if (sscanf(name, "wide_mt%d_nt%d_w%d_d%d_split%d%n", &mt, &nt, &w, &d, &split, &used) != 5 || name[used] != 0)
+      return false;
+    v = find_gemm_variant(mt, nt, 1, w, d, 1, 16, 1);
+  } else {
+    if (sscanf(name, "mt%d_nt%d_wn%d_wk%d_kpw%d_split%d%n", &mt, &nt, &wn, &wk, &kpw, &split, &used) != 6)
+      return false;
+    int pq = 0, rb = 16;
+    const char *rest = name + used;
+    if (strcmp(rest, "_pq") == 0) {
+      pq = 1;
+    } else if (strcmp(rest, "_r8") == 0) {
+      rb = 8;
+    } else if (*rest != 0) {
+      return false;
+    }
+    v = find_gemm_variant(mt, nt, wn, wk, kpw, pq, rb, 0);
   }
-  const int v = find_gemm_variant(mt, nt, wn, wk, kpw, pq, rb);
   if (v < 0 || split < 1) return false;
   gemm_variant_shape(v, out);
   out->split = split;
@@ -247,8 +277,11 @@ const char *mxfp4_gemm_schedule_name(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 1 || K % 64 != 0 || N % 32 != 0) return nullptr;
   Schedule s;
   if (!choose((int)M, (int)N, (int)K, &s)) return nullptr;
-  snprintf(buf, sizeof(buf), "mt%d_nt%d_wn%d_wk%d_kpw%d_split%d%s", s.mt, s.nt, s.wn, s.wk, s.kpw, s.split,
-           s.pq ? "_pq" : (s.rb == 8 ? "_r8" : ""));
+  if (s.wide)
+    snprintf(buf, sizeof(buf), "wide_mt%d_nt%d_w%d_d%d_split%d", s.mt, s.nt, s.wk, s.kpw, s.split);
+  else
+    snprintf(buf, sizeof(buf), "mt%d_nt%d_wn%d_wk%d_kpw%d_split%d%s", s.mt, s.nt, s.wn, s.wk, s.kpw, s.split,
+             s.pq ? "_pq" : (s.rb == 8 ? "_r8" : ""));
   return buf;
 }
 

@@ -14,6 +14,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Scale byte of a group from the largest |x| given as bf16 magnitude bits
 // (15 bits, sign cleared).  The f32 pattern of amax is those bits << 16.
@@ -125,6 +126,57 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 __device__ __forceinline__ uint32_t shuffled_scale_offset(uint32_t row, uint32_t g, uint32_t gp) {
   uint32_t in_block = ((row >> 4) & 1u) | (((g >> 2) & 1u) << 1) | ((row & 15u) << 2) | ((g & 3u) << 6);
   return in_block + ((g >> 3) << 8) + (row >> 5) * 32u * gp;
+}
+
+// Word 3 of a gfx9 buffer resource for raw (untyped) dword access.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// Buffer offset that reads zeros unless `in_range`: a buffer load past the
+// descriptor's size returns zeros, and every offset used with these
+// descriptors is below 2^31, so setting bit 31 puts it out of range.  An OR
+// with a select of two constants keeps the compiler from turning the choice
+// into a branch around the load (which would force a wait for every
+// outstanding load where the paths meet).
+__device__ __forceinline__ int off_or_oob(bool in_range, int off) {
+  return off | (in_range ? 0 : (int)0x80000000u);
+}
+
+// DPP lane patterns within groups of four lanes.
+constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadSwap1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kQuadSwap2, 0xF, 0xF, false));
+  return v;
+}
+
+// Quantize 8 consecutive elements of a 32-element group (4 dwords of bf16
+// pairs) whose other 24 elements sit in the three neighbouring lanes of the
+// same quad: returns the lane's dword of codes and writes the scale byte.
+__device__ __forceinline__ uint32_t quant_quarter(const u32x4 &w, int sw_quant, uint32_t *scale) {
+  u16x2 m = __builtin_bit_cast(u16x2, w.x & 0x7FFF7FFFu);
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.y & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.z & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.w & 0x7FFF7FFFu));
+  const uint32_t amax = quad_max(m.x > m.y ? m.x : m.y);
+  const uint32_t s = scale_byte_from_amax(amax);
+  *scale = s;
+  uint32_t d = 0;
+  if (!sw_quant) {
+    const float sf = __uint_as_float(s << 23);
+    d = cvt_pair_hw<0>(d, w.x, sf);
+    d = cvt_pair_hw<1>(d, w.y, sf);
+    d = cvt_pair_hw<2>(d, w.z, sf);
+    d = cvt_pair_hw<3>(d, w.w, sf);
+  } else {
+    const float inv = inv_scale_f32(s);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      d |= (encode_sw(ww[b] & 0xFFFFu, inv) | (encode_sw(ww[b] >> 16, inv) << 4)) << (8 * b);
+  }
+  return d;
 }
 
 }  // namespace mxfp4

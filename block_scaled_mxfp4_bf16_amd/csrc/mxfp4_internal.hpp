@@ -19,8 +19,11 @@ namespace mxfp4 {
 //         the workspace and the GEMM reads those; 0: the GEMM quantizes A
 //   rb    rows per staged A block: 16, or 8 (for M <= 8: no loads or
 //         converts are spent on rows that do not exist)
+//   wide  1: the large-M kernel -- A quantized once, wk waves per
+//         workgroup that split K, each holding the whole 16*mt x 16*nt
+//         tile; kpw is then the number of K steps loaded ahead
 struct Schedule {
-  int mt, nt, wn, wk, kpw, split, pq, rb;
+  int mt, nt, wn, wk, kpw, split, pq, rb, wide;
   int variant;  // index into the kernel table
 };
 
@@ -43,7 +46,27 @@ struct GemmArgs {
 // Kernel table queries (gemm_kernels.hip).
 int num_gemm_variants();
 void gemm_variant_shape(int v, Schedule *s);  // fills everything but split
-int find_gemm_variant(int mt, int nt, int wn, int wk, int kpw, int pq, int rb);
+int find_gemm_variant(int mt, int nt, int wn, int wk, int kpw, int pq, int rb, int wide);
+
+// Bytes of pre-quantized A in the workspace: the larger of the two operand
+// layouts (the fused kernels' 1088-byte blocks, the large-M kernel's
+// quad-packed one), so one workspace size serves either.
+size_t operand_a_bytes(int M, int K);
+size_t quad_operand_bytes(int M, int K);
+inline size_t pq_operand_bytes(int M, int K) {
+  const size_t a = operand_a_bytes(M, K), b = quad_operand_bytes(M, K);
+  return a > b ? a : b;
+}
+
+// Large-M kernels compiled (gemm_wide.hip): (row tiles, column subtiles,
+// waves, K steps loaded ahead).
+#define MXFP4_WIDE_VARIANTS(X)                                                                          \
+  X(4, 7, 8, 2) X(4, 7, 4, 2) X(4, 8, 8, 2) X(4, 6, 8, 2) X(4, 4, 8, 2) X(4, 4, 8, 3) X(4, 3, 8, 2) \
+  X(4, 3, 8, 3) X(4, 2, 8, 2) X(4, 2, 8, 4) X(4, 1, 8, 4) X(8, 2, 8, 2) X(8, 3, 8, 2)
+#define MXFP4_DECLARE_WIDE(MW, NW, W, D) \
+  hipError_t launch_wide_##MW##_##NW##_##W##_##D(const GemmArgs &a, int split, bool sw, hipStream_t stream);
+MXFP4_WIDE_VARIANTS(MXFP4_DECLARE_WIDE)
+#undef MXFP4_DECLARE_WIDE
 
 size_t gemm_workspace_bytes(const Schedule &s, int M, int N, int K);
 hipError_t launch_gemm(const Schedule &s, const GemmArgs &a, bool sw_quant, hipStream_t stream);

@@ -131,8 +131,38 @@ def test_eight_row_schedules_only_cover_m_up_to_8():
     assert not mx.mxfp4_gemm_schedule_name(9, 512, 1024).endswith("_r8")
 
 
+def test_wide_schedule_names():
+    assert mx.mxfp4_gemm_schedule_name(256, 7168, 7168).startswith("wide_")
+    mx.mxfp4_set_schedule_override("wide_mt4_nt7_w8_d2_split2")
+    try:
+        assert mx.mxfp4_gemm_schedule_name(256, 7168, 7168) == "wide_mt4_nt7_w8_d2_split2"
+        assert mx.mxfp4_gemm_schedule_name(256, 7168 - 32, 7168) is None  # N not a multiple of 112
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+    for bad in ("wide_mt4_nt7_w8_d9_split1", "wide_mt3_nt7_w8_d2_split1", "wide_mt4_nt7_w8_d2_split1_pq", "wide_mt4_nt7_d2_split1"):
+        with pytest.raises(RuntimeError):
+            mx.mxfp4_set_schedule_override(bad)
+
+
 def test_quant_mode_knob():
     with pytest.raises(RuntimeError):
         mx.mxfp4_set_quant_mode(2)
     mx.mxfp4_set_quant_mode(1)
     mx.mxfp4_set_quant_mode(0)
+
+
+def test_every_schedule_the_gpu_tests_name_covers_its_shape():
+    """The GPU tests force schedules by name; each must resolve for the
+    shape it is used with (checked here so that a typo fails on the CPU)."""
+    from tests import test_gpu_gemm as g
+    cases = [(s, M, N, K) for s, M, N, K in g.WIDE_CASES]
+    cases += [(s, M, 256, 2048 + 64) for s in g.R8_SCHEDULES for M in (1, 5, 8)]
+    cases += [(s, 70, 224, 1088) for s in ("wide_mt4_nt7_w4_d2_split1", "wide_mt8_nt2_w8_d2_split2")]
+    try:
+        for s in g.SCHEDULES:  # compiled (the test skips those that cannot cover its K)
+            mx.mxfp4_set_schedule_override(s)
+        for s, M, N, K in cases:
+            mx.mxfp4_set_schedule_override(s)
+            assert mx.mxfp4_gemm_schedule_name(M, N, K) == s, (s, M, N, K)
+    finally:
+        mx.mxfp4_set_schedule_override(None)

@@ -120,8 +120,8 @@ SCHEDULES = ["mt1_nt1_wn1_wk1_kpw1_split17", "mt1_nt1_wn1_wk4_kpw1_split5", "mt1
              # A quantized once by its own launch into operand blocks
              "mt4_nt2_wn2_wk2_kpw4_split3_pq", "mt1_nt1_wn2_wk8_kpw1_split3_pq", "mt8_nt1_wn2_wk2_kpw4_split3_pq",
              "mt2_nt2_wn1_wk1_kpw4_split5_pq", "mt4_nt4_wn1_wk2_kpw4_split3_pq",
-             # K-loop kernels (pre-quantized A staged through LDS)
-             "mt4_nt2_wn4_wk0_kpw2_split1_pq", "mt8_nt1_wn2_wk0_kpw4_split3_pq", "mt2_nt4_wn1_wk0_kpw2_split2_pq"]
+             # large-M kernel: waves split K, A quantized once
+             "wide_mt4_nt2_w8_d2_split1", "wide_mt4_nt4_w8_d3_split3", "wide_mt8_nt2_w8_d2_split2"]
 
 
 @pytest.mark.parametrize("sched", SCHEDULES)
@@ -193,10 +193,11 @@ def test_workspace_reused_across_shapes_with_more_tiles():
     assert_close(first.run(), first.ref(), "first shape again")
 
 
-@pytest.mark.parametrize("sched", ["mt4_nt1_wn7_wk0_kpw4_split1_pq", "mt8_nt1_wn2_wk0_kpw2_split2_pq"])
+@pytest.mark.parametrize("sched", ["wide_mt4_nt7_w4_d2_split1", "wide_mt8_nt2_w8_d2_split2"])
 def test_k_loop_kernels_ragged(sched):
-    """K loop with a step count that is not a multiple of the prefetch depth,
-    a half step (K % 128 == 64), and rows past the last full M tile."""
+    """K loop with a step count that is not a multiple of the prefetch depth
+    or of the waves, a half step (K % 128 == 64), and rows past the last
+    full row tile."""
     torch = torch_cuda()
     c = make(torch, 70, 224, 1088, seed=9)
     mx.mxfp4_set_schedule_override(sched)
@@ -230,3 +231,28 @@ def test_eight_row_staging_matches_oracle(sched, M):
         mx.mxfp4_set_schedule_override(None)
     assert np.array_equal(first, second)
     assert_close(first, c.ref(), "%s M=%d" % (sched, M))
+
+
+# Large-M kernel: (schedule, M, N, K) with partial row tiles, row tiles past
+# the quantized quads, half steps at the end of K, and uneven K splits.
+WIDE_CASES = [("wide_mt4_nt7_w8_d2_split1", 130, 224, 1088), ("wide_mt4_nt7_w4_d2_split3", 70, 448, 2112),
+              ("wide_mt8_nt2_w8_d2_split2", 200, 128, 1600), ("wide_mt8_nt2_w8_d2_split1", 129, 96, 640),
+              ("wide_mt4_nt3_w8_d3_split1", 256, 192, 512), ("wide_mt4_nt6_w8_d2_split4", 96, 192, 4096),
+              ("wide_mt4_nt2_w8_d4_split1", 17, 64, 256), ("wide_mt4_nt4_w8_d3_split1", 256, 512, 1024),
+              ("wide_mt4_nt8_w8_d2_split5", 80, 256, 2112), ("wide_mt4_nt1_w8_d4_split3", 64, 96, 448),
+              ("wide_mt8_nt3_w8_d2_split1", 140, 96, 8192), ("wide_mt4_nt4_w8_d2_split2", 66, 64, 64)]
+
+
+@pytest.mark.parametrize("sched,M,N,K", WIDE_CASES)
+def test_wide_kernel_matches_oracle(sched, M, N, K):
+    torch = torch_cuda()
+    c = make(torch, M, N, K, seed=M + N + K)
+    mx.mxfp4_set_schedule_override(sched)
+    try:
+        assert mx.mxfp4_gemm_schedule_name(c.M, c.N, c.K) == sched
+        first = c.run()
+        second = c.run()
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+    assert np.array_equal(first, second)
+    assert_close(first, c.ref(), "%s %dx%dx%d" % (sched, M, N, K))
