@@ -37,6 +37,8 @@
 // partials in split order, stores bf16 C and resets the ticket.  The sum
 // order is fixed, so results are deterministic, and there is no second
 // launch (the pages reduce split-K partials with a second kernel).
+#include <type_traits>
+
 #include "mxfp4_device.hpp"
 #include "mxfp4_internal.hpp"
 
@@ -160,27 +162,35 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
     }
   }
 
-  // Phase 2: quantize the staged A blocks into LDS.
+  // Phase 2: quantize the staged A blocks into LDS (the encoder is chosen
+  // once for all blocks, so the hardware path is straight-line code).
   if constexpr (!PREQ) {
+    auto stage_all = [&](auto sw_tag) {
+      constexpr bool SW = decltype(sw_tag)::value;
 #pragma unroll
-    for (int u = 0; u < UPW; ++u) {
-      const int unit = WN == 1 ? wk * (KPW * MT * UPS) + u : wave + u * WAVES;
-      if (UPW * WAVES == UNITS || unit < UNITS) {
-        uint32_t s;
-        const uint32_t d = quant_quarter(aw[u], sw_quant, &s);
-        if constexpr (RB == 8) {
-          // lane t: row t/8, chunk 2*(unit&1) + (t/4)%2, quarter t%4
-          const int blk = unit >> 1;
-          const int ch = 2 * (unit & 1) + ((lane >> 2) & 1);
-          const int r = lane >> 3;
-          a_lds[blk * 256 + ch * 64 + r * 4 + (lane & 3)] = d;
-          if ((lane & 3) == 0) s_lds[blk * 64 + ch * 16 + r] = (uint8_t)s;
-        } else {
-          a_lds[unit * 64 + lane] = d;
-          if ((lane & 3) == 0) s_lds[(unit >> 2) * 64 + (unit & 3) * 16 + (lane >> 2)] = (uint8_t)s;
+      for (int u = 0; u < UPW; ++u) {
+        const int unit = WN == 1 ? wk * (KPW * MT * UPS) + u : wave + u * WAVES;
+        if (UPW * WAVES == UNITS || unit < UNITS) {
+          uint32_t s;
+          const uint32_t d = quant_quarter_t<SW>(aw[u], &s);
+          if constexpr (RB == 8) {
+            // lane t: row t/8, chunk 2*(unit&1) + (t/4)%2, quarter t%4
+            const int blk = unit >> 1;
+            const int ch = 2 * (unit & 1) + ((lane >> 2) & 1);
+            const int r = lane >> 3;
+            a_lds[blk * 256 + ch * 64 + r * 4 + (lane & 3)] = d;
+            if ((lane & 3) == 0) s_lds[blk * 64 + ch * 16 + r] = (uint8_t)s;
+          } else {
+            a_lds[unit * 64 + lane] = d;
+            if ((lane & 3) == 0) s_lds[(unit >> 2) * 64 + (unit & 3) * 16 + (lane >> 2)] = (uint8_t)s;
+          }
         }
       }
-    }
+    };
+    if (sw_quant)
+      stage_all(std::true_type{});
+    else
+      stage_all(std::false_type{});
     if constexpr (WN == 1) {
       // the blocks this wave reads are the ones it wrote: LDS keeps one
       // wave's accesses in order, so only the compiler must not reorder

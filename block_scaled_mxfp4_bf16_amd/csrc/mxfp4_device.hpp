@@ -154,7 +154,8 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
 // Quantize 8 consecutive elements of a 32-element group (4 dwords of bf16
 // pairs) whose other 24 elements sit in the three neighbouring lanes of the
 // same quad: returns the lane's dword of codes and writes the scale byte.
-__device__ __forceinline__ uint32_t quant_quarter(const u32x4 &w, int sw_quant, uint32_t *scale) {
+template <bool SW>
+__device__ __forceinline__ uint32_t quant_quarter_t(const u32x4 &w, uint32_t *scale) {
   u16x2 m = __builtin_bit_cast(u16x2, w.x & 0x7FFF7FFFu);
   m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.y & 0x7FFF7FFFu));
   m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w.z & 0x7FFF7FFFu));
@@ -163,7 +164,7 @@ __device__ __forceinline__ uint32_t quant_quarter(const u32x4 &w, int sw_quant, 
   const uint32_t s = scale_byte_from_amax(amax);
   *scale = s;
   uint32_t d = 0;
-  if (!sw_quant) {
+  if constexpr (!SW) {
     const float sf = __uint_as_float(s << 23);
     d = cvt_pair_hw<0>(d, w.x, sf);
     d = cvt_pair_hw<1>(d, w.y, sf);
@@ -177,6 +178,12 @@ __device__ __forceinline__ uint32_t quant_quarter(const u32x4 &w, int sw_quant, 
       d |= (encode_sw(ww[b] & 0xFFFFu, inv) | (encode_sw(ww[b] >> 16, inv) << 4)) << (8 * b);
   }
   return d;
+}
+
+// Runtime choice of encoder for one call site; kernels that quantize many
+// quarters branch once around a loop of quant_quarter_t instead.
+__device__ __forceinline__ uint32_t quant_quarter(const u32x4 &w, int sw_quant, uint32_t *scale) {
+  return sw_quant ? quant_quarter_t<true>(w, scale) : quant_quarter_t<false>(w, scale);
 }
 
 }  // namespace mxfp4
