@@ -29,8 +29,10 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 matrix peak, TFLOP/s
 HEADLINE = "c2"
+# What decides the headline GEMM's code: its kernel sources, plus the
+# schedule the library picks for the headline shape (hashed with them).
 KERNEL_SOURCES = ["block_scaled_mxfp4_bf16_amd/csrc/gemm_kernels.hip", "block_scaled_mxfp4_bf16_amd/csrc/mxfp4_device.hpp",
-                  "block_scaled_mxfp4_bf16_amd/csrc/mxfp4_api.hip"]
+                  "block_scaled_mxfp4_bf16_amd/csrc/mxfp4_internal.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_M32_N4096_K512.json")
 CALIBRATION_BYTES = 256 << 20
 
@@ -53,10 +55,14 @@ def calibration_copy(torch):
 
 def kernel_source_hash():
     import hashlib
+    import block_scaled_mxfp4_bf16_amd as mx
+    import synthetic as syn
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    w = syn.CONFIGS[HEADLINE]
+    h.update(str(mx.mxfp4_gemm_schedule_name(w.M, w.N, w.K)).encode())
     return h.hexdigest()[:16]
 
 
@@ -148,6 +154,43 @@ def time_config(torch, mx, w, steps, warmup, cold):
     }
 
 
+def time_prepare_b(torch, mx, w, steps=50):
+    """One-launch B preparation (quantize + both shuffles) of a workload's B,
+    cold: consecutive calls cycle through >= 1 GiB of bf16 B copies."""
+    import numpy as np
+    N, K = w.N, w.K
+    b = torch.from_numpy(w.b_bits().view(np.int16)).view(torch.bfloat16).to("cuda")
+    sets = max(2, math.ceil((1 << 30) / (2 * N * K)))
+    bs_in = [b] + [b.clone() for _ in range(sets - 1)]
+    bw = torch.empty((N // 16, (K // 2) * 16), dtype=torch.uint8, device="cuda")
+    bs = torch.empty(mx.mxfp4_shuffled_scale_bytes(N, K), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            mx.mxfp4_prepare_b(bs_in[i % sets], N, K, bw, bs, stream=stream)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(steps):
+            mx.mxfp4_prepare_b(bs_in[i % sets], N, K, bw, bs, stream=stream)
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / steps
+    nbytes = 2 * N * K + N * K // 2 + mx.mxfp4_shuffled_scale_bytes(N, K)
+    del g, bs_in, b
+    torch.cuda.empty_cache()
+    return {"N": N, "K": K, "us_per_call": round(us, 3), "bytes": nbytes, "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "buffer_sets": sets}
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The oracle as it stands, single-threaded, on whole calls of the
     headline workload (quantize A, exact GEMM, round) until the budget is
@@ -229,6 +272,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--configs", default="c1,c2,c3,c4,c5", help="configurations measured under per_config")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-b-prep", action="store_true", help="skip timing the one-launch B preparation")
     ap.add_argument("--warm", action="store_true", help="also time with one buffer set (caches warm)")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="first run a cold 256 MiB device copy (for scaling HBM counters)")
@@ -291,6 +335,16 @@ def main():
         },
         "per_config": per,
     }
+    if not args.no_b_prep:
+        # offline weight preparation (not part of a call): its own throughput
+        line["b_prep"] = {}
+        for name in ("c2", "c5"):
+            w = syn.CONFIGS[name]
+            r = time_prepare_b(torch, mx, w)
+            line["b_prep"][w.name] = r
+            print("[bench] B prep %dx%d: %.2f us, %.0f GB/s (%.1f%% of HBM)" % (w.N, w.K, r["us_per_call"], r["gbs"],
+                                                                           100 * r["hbm_frac"]),
+                  file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(hw)
     print(json.dumps(line), flush=True)

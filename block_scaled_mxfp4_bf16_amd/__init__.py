@@ -25,6 +25,16 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
+    # PyTorch ships its own HIP runtime and asks for it as "libamdhip64.so";
+    # this library asks for "libamdhip64.so.7", the soname that copy carries.
+    # Loaded after torch, this library therefore binds to torch's runtime.
+    # Loaded first, it would bring in /opt/rocm's copy and torch would then
+    # load a second one, and the two runtimes in one process do not share
+    # the device.  So torch goes first whenever it is installed.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(
             "libmxfp4.so is not built (expected at %s); run __graft_entry__.build() or "
@@ -38,10 +48,12 @@ def _load():
         "mxfp4_gemm_workspace_bytes": (SZ, [I64, I64, I64]),
         "mxfp4_quantize": (I, [P, I64, I64, P, P, I, P]),
         "mxfp4_preshuffle_b": (I, [P, P, I64, I64, P, P, P]),
+        "mxfp4_prepare_b": (I, [P, I64, I64, P, P, P]),
         "mxfp4_gemm": (I, [P, P, P, P, I64, I64, I64, P]),
         "mxfp4_gemm_ex": (I, [P, P, P, P, I64, I64, I64, P, SZ, P]),
         "mxfp4_reserve": (I, [I64, I64, I64, P]),
         "mxfp4_status_string": (ctypes.c_char_p, [I]),
+        "mxfp4_last_hip_error": (ctypes.c_char_p, []),
         "mxfp4_gemm_schedule_name": (ctypes.c_char_p, [I64, I64, I64]),
         "mxfp4_set_quant_mode": (I, [I]),
         "mxfp4_set_schedule_override": (I, [ctypes.c_char_p]),
@@ -61,14 +73,17 @@ def lib():
 def exported_symbols():
     """Names every entry point the header declares (used by the ABI test)."""
     return ["mxfp4_packed_bytes", "mxfp4_raw_scale_bytes", "mxfp4_shuffled_scale_bytes",
-            "mxfp4_gemm_workspace_bytes", "mxfp4_quantize", "mxfp4_preshuffle_b", "mxfp4_gemm",
-            "mxfp4_gemm_ex", "mxfp4_reserve", "mxfp4_status_string", "mxfp4_gemm_schedule_name",
+            "mxfp4_gemm_workspace_bytes", "mxfp4_quantize", "mxfp4_preshuffle_b", "mxfp4_prepare_b", "mxfp4_gemm",
+            "mxfp4_gemm_ex", "mxfp4_reserve", "mxfp4_status_string", "mxfp4_last_hip_error", "mxfp4_gemm_schedule_name",
             "mxfp4_set_quant_mode", "mxfp4_set_schedule_override"]
 
 
 def _check(rc: int, what: str):
     if rc != MXFP4_OK:
-        msg = _load().mxfp4_status_string(rc).decode()
+        L = _load()
+        msg = L.mxfp4_status_string(rc).decode()
+        if rc == 4:  # MXFP4_ERR_HIP: name the HIP error
+            msg += " (%s)" % L.mxfp4_last_hip_error().decode()
         raise RuntimeError("%s failed: %s" % (what, msg))
 
 
@@ -124,6 +139,11 @@ def mxfp4_preshuffle_b(bq, bs_raw, N: int, K: int, bq_shuffled, bs_shuffled, str
                                       _stream(stream)), "mxfp4_preshuffle_b")
 
 
+def mxfp4_prepare_b(b, N: int, K: int, bq_shuffled, bs_shuffled, stream=None):
+    _check(_load().mxfp4_prepare_b(_ptr(b), N, K, _ptr(bq_shuffled), _ptr(bs_shuffled), _stream(stream)),
+           "mxfp4_prepare_b")
+
+
 def mxfp4_gemm(A, Bq_sh, Bs_sh, C, M: int, N: int, K: int, stream=None):
     _check(_load().mxfp4_gemm(_ptr(A), _ptr(Bq_sh), _ptr(Bs_sh), _ptr(C), M, N, K, _stream(stream)), "mxfp4_gemm")
 
@@ -171,6 +191,18 @@ def preshuffle_b(bq, bs_raw, stream=None):
     bs = torch.empty(mxfp4_shuffled_scale_bytes(N, K), dtype=torch.uint8, device=bq.device)
     bs = bs.view(-1, ((K // 32 + 7) // 8) * 32)
     mxfp4_preshuffle_b(bq, bs_raw, N, K, bw, bs, stream)
+    return bw, bs
+
+
+def prepare_b(b, stream=None):
+    """bf16 [N, K] cuda tensor -> (Bw [N/16, (K/2)*16], Bs shuffled), in one launch."""
+    import torch
+    N, K = b.shape
+    assert b.dtype == torch.bfloat16 and b.is_contiguous()
+    bw = torch.empty((N // 16, (K // 2) * 16), dtype=torch.uint8, device=b.device)
+    bs = torch.empty(mxfp4_shuffled_scale_bytes(N, K), dtype=torch.uint8, device=b.device)
+    bs = bs.view(-1, ((K // 32 + 7) // 8) * 32)
+    mxfp4_prepare_b(b, N, K, bw, bs, stream)
     return bw, bs
 
 

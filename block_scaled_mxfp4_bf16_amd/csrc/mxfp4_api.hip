@@ -17,6 +17,15 @@ namespace {
 
 const int64_t kMaxBytes = (int64_t)1 << 31;  // 32-bit offsets inside the kernels
 
+// The last HIP error this thread's calls into the library met.
+thread_local hipError_t t_last_hip_error = hipSuccess;
+
+mxfp4_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return MXFP4_OK;
+  t_last_hip_error = e;
+  return MXFP4_ERR_HIP;
+}
+
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 inline int64_t pad_to(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
@@ -205,7 +214,7 @@ mxfp4_status_t get_workspace(size_t need, hipStream_t stream, void **out) {
   *out = nullptr;
   if (need == 0) return MXFP4_OK;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return MXFP4_ERR_HIP;
+  if (hipError_t e0 = hipGetDevice(&dev); e0 != hipSuccess) return hip_status(e0);
   std::lock_guard<std::mutex> lk(g_ws_mu);
   for (auto &e : g_ws) {
     if (e.device == dev && e.stream == (void *)stream) {
@@ -214,22 +223,22 @@ mxfp4_status_t get_workspace(size_t need, hipStream_t stream, void **out) {
         return MXFP4_OK;
       }
       // grow: wait for work that may still use the old buffer
-      if (hipStreamSynchronize(stream) != hipSuccess) return MXFP4_ERR_HIP;
-      if (hipFree(e.ptr) != hipSuccess) return MXFP4_ERR_HIP;
+      if (hipError_t e0 = hipStreamSynchronize(stream); e0 != hipSuccess) return hip_status(e0);
+      if (hipError_t e0 = hipFree(e.ptr); e0 != hipSuccess) return hip_status(e0);
       e.ptr = nullptr;
       e.bytes = 0;
-      if (hipMalloc(&e.ptr, need) != hipSuccess) return MXFP4_ERR_HIP;
-      if (hipMemsetAsync(e.ptr, 0, need, stream) != hipSuccess) return MXFP4_ERR_HIP;
+      if (hipError_t e0 = hipMalloc(&e.ptr, need); e0 != hipSuccess) return hip_status(e0);
+      if (hipError_t e0 = hipMemsetAsync(e.ptr, 0, need, stream); e0 != hipSuccess) return hip_status(e0);
       e.bytes = need;
       *out = e.ptr;
       return MXFP4_OK;
     }
   }
   WsEntry e{dev, (void *)stream, nullptr, 0};
-  if (hipMalloc(&e.ptr, need) != hipSuccess) return MXFP4_ERR_HIP;
-  if (hipMemsetAsync(e.ptr, 0, need, stream) != hipSuccess) {
+  if (hipError_t e0 = hipMalloc(&e.ptr, need); e0 != hipSuccess) return hip_status(e0);
+  if (hipError_t e0 = hipMemsetAsync(e.ptr, 0, need, stream); e0 != hipSuccess) {
     (void)hipFree(e.ptr);
-    return MXFP4_ERR_HIP;
+    return hip_status(e0);
   }
   e.bytes = need;
   g_ws.push_back(e);
@@ -270,6 +279,10 @@ const char *mxfp4_status_string(mxfp4_status_t st) {
     case MXFP4_ERR_HIP: return "MXFP4_ERR_HIP: a HIP call or kernel launch failed";
   }
   return "MXFP4: unknown status";
+}
+
+const char *mxfp4_last_hip_error(void) {
+  return t_last_hip_error == hipSuccess ? "hipSuccess" : hipGetErrorName(t_last_hip_error);
 }
 
 const char *mxfp4_gemm_schedule_name(int64_t M, int64_t N, int64_t K) {
@@ -315,7 +328,7 @@ mxfp4_status_t mxfp4_quantize(const void *x_bf16, int64_t rows, int64_t K, void 
   if (K % 32 != 0) return MXFP4_ERR_UNSUPPORTED;
   if (rows * K * 2 >= kMaxBytes || pad_to(rows, 256) * pad_to(K / 32, 8) >= kMaxBytes) return MXFP4_ERR_UNSUPPORTED;
   hipError_t e = launch_quantize(x_bf16, rows, K, q, scales, shuffled_scales != 0, sw_quant(), (hipStream_t)stream);
-  return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+  return hip_status(e);
 }
 
 mxfp4_status_t mxfp4_preshuffle_b(const void *bq, const void *bs_raw, int64_t N, int64_t K, void *bq_shuffled,
@@ -326,7 +339,18 @@ mxfp4_status_t mxfp4_preshuffle_b(const void *bq, const void *bs_raw, int64_t N,
   if (N % 16 != 0 || K % 32 != 0) return MXFP4_ERR_UNSUPPORTED;
   if (N * K / 2 >= kMaxBytes || pad_to(N, 256) * pad_to(K / 32, 8) >= kMaxBytes) return MXFP4_ERR_UNSUPPORTED;
   hipError_t e = launch_preshuffle_b(bq, bs_raw, N, K, bq_shuffled, bs_shuffled, (hipStream_t)stream);
-  return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+  return hip_status(e);
+}
+
+mxfp4_status_t mxfp4_prepare_b(const void *b_bf16, int64_t N, int64_t K, void *bq_shuffled, void *bs_shuffled,
+                               mxfp4_stream_t stream) {
+  if (!b_bf16 || !bq_shuffled || !bs_shuffled) return MXFP4_ERR_INVALID_ARG;
+  if (N < 1 || K < 32) return MXFP4_ERR_INVALID_ARG;
+  if (!aligned(b_bf16, 16) || !aligned(bq_shuffled, 16)) return MXFP4_ERR_INVALID_ARG;
+  if (N % 16 != 0 || K % 32 != 0) return MXFP4_ERR_UNSUPPORTED;
+  if (N * K * 2 >= kMaxBytes || pad_to(N, 256) * pad_to(K / 32, 8) >= kMaxBytes) return MXFP4_ERR_UNSUPPORTED;
+  hipError_t e = launch_prepare_b(b_bf16, N, K, bq_shuffled, bs_shuffled, sw_quant(), (hipStream_t)stream);
+  return hip_status(e);
 }
 
 mxfp4_status_t mxfp4_gemm_ex(const void *A, const void *Bq_sh, const void *Bs_sh, void *C, int64_t M, int64_t N,
@@ -338,7 +362,7 @@ mxfp4_status_t mxfp4_gemm_ex(const void *A, const void *Bq_sh, const void *Bs_sh
   const size_t need = gemm_workspace_bytes(s, (int)M, (int)N, (int)K);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return MXFP4_ERR_WORKSPACE;
   GemmArgs a{A, Bq_sh, Bs_sh, C, workspace, (int)M, (int)N, (int)K};
-  return launch_gemm(s, a, sw_quant(), (hipStream_t)stream) == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+  return hip_status(launch_gemm(s, a, sw_quant(), (hipStream_t)stream));
 }
 
 mxfp4_status_t mxfp4_gemm(const void *A, const void *Bq_sh, const void *Bs_sh, void *C, int64_t M, int64_t N,
@@ -352,7 +376,7 @@ mxfp4_status_t mxfp4_gemm(const void *A, const void *Bq_sh, const void *Bs_sh, v
   st = get_workspace(need, (hipStream_t)stream, &ws);
   if (st != MXFP4_OK) return st;
   GemmArgs a{A, Bq_sh, Bs_sh, C, ws, (int)M, (int)N, (int)K};
-  return launch_gemm(s, a, sw_quant(), (hipStream_t)stream) == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+  return hip_status(launch_gemm(s, a, sw_quant(), (hipStream_t)stream));
 }
 
 mxfp4_status_t mxfp4_reserve(int64_t M, int64_t N, int64_t K, mxfp4_stream_t stream) {

@@ -75,5 +75,6 @@ hipError_t launch_quantize(const void *x, int64_t rows, int64_t K, void *q, void
                            hipStream_t stream);
 hipError_t launch_preshuffle_b(const void *bq, const void *bs_raw, int64_t N, int64_t K, void *bq_sh, void *bs_sh,
                                hipStream_t stream);
+hipError_t launch_prepare_b(const void *b, int64_t N, int64_t K, void *bq_sh, void *bs_sh, bool sw, hipStream_t stream);
 
 }  // namespace mxfp4

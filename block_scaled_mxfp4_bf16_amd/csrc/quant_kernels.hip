@@ -4,6 +4,7 @@
 //   quantize_shuffled same codes; scales written in the shuffled, padded layout
 //   preshuffle_b_data packed e2m1 [N, K/2] -> 16x16-byte tile layout
 //   shuffle_scales    raw e8m0 [N, K/32] -> shuffled, padded layout
+//   prepare_b         bf16 [N, K] -> both GEMM layouts of B in one pass
 //
 // One lane owns one 32-element group: a 64-byte load, the group scale, 16
 // converts and a 16-byte store; nothing crosses lanes.  These kernels prepare
@@ -92,6 +93,52 @@ __global__ __launch_bounds__(256) void shuffle_scales_kernel(const uint8_t *__re
   out[a] = (row < rows && g < G) ? raw[row * G + g] : (uint8_t)127;
 }
 
+// Quantize B and write it straight into the GEMM's layouts (the pages
+// prepare B offline with a quantize, then a shuffle of codes and scales).
+// One single-wave workgroup per (16-row group g, 128-wide step s) of the
+// padded scale layout, g < pad256(N)/16, s < pad8(K/32)/4.  Each of its
+// four loads covers the 16 rows x one 32-element group (four lanes per
+// group, coalesced); lane t = 4r + q then holds bytes 4q..4q+3 of row r in
+// tile t' = 4s + ch of the preshuffled layout, so the 64 lanes' dwords are
+// one contiguous 256-byte tile.  Rows past N and groups past K/32 load as
+// zeros, write no codes and get the scale fill byte 127.
+template <bool SW>
+__global__ __launch_bounds__(64) void prepare_b_kernel(const uint16_t *__restrict__ B, uint8_t *__restrict__ bq_sh,
+                                                       uint8_t *__restrict__ bs_sh, int N, int K, int gp) {
+  const int lane = threadIdx.x;
+  const int steps = gp >> 2;
+  const int g = blockIdx.x / steps, s = blockIdx.x - (blockIdx.x / steps) * steps;
+  const int G = K >> 5;
+  const int rows_p = (N + 255) & ~255;
+  const int b_bytes = N * K * 2;
+  const int q_bytes = N * (K >> 1);
+  const int s_bytes = rows_p * gp;
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)B, 0, b_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)bq_sh, 0, q_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)bs_sh, 0, s_bytes, kRsrcWord3);
+  const int row = 16 * g + (lane >> 2);
+  u32x4 w[4];
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) {
+    const int grp = 4 * s + ch;
+    const bool ok = row < N && grp < G;
+    w[ch] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, off_or_oob(ok, (row * K + grp * 32 + (lane & 3) * 8) * 2), 0,
+                                                  0);
+  }
+#pragma unroll
+  for (int ch = 0; ch < 4; ++ch) {
+    const int grp = 4 * s + ch;
+    uint32_t sc;
+    const uint32_t d = quant_quarter_t<SW>(w[ch], &sc);
+    const bool codes = 16 * g < N && grp < G;
+    __builtin_amdgcn_raw_buffer_store_b32(d, q_rsrc, off_or_oob(codes, g * (K >> 1) * 16 + grp * 256 + lane * 4), 0,
+                                          0);
+    const uint32_t byte = (row < N && grp < G) ? sc : 127u;
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, s_rsrc,
+                                         off_or_oob((lane & 3) == 0, (int)shuffled_scale_offset(row, grp, gp)), 0, 0);
+  }
+}
+
 static inline uint32_t blocks_for(uint64_t n) { return (uint32_t)((n + 255) / 256); }
 
 hipError_t launch_quantize(const void *x, int64_t rows, int64_t K, void *q, void *scales, bool shuffled, bool sw,
@@ -131,6 +178,19 @@ hipError_t launch_preshuffle_b(const void *bq, const void *bs_raw, int64_t N, in
   uint32_t total = (uint32_t)((N + 255) / 256 * 256) * gp;
   shuffle_scales_kernel<<<blocks_for(total), 256, 0, stream>>>((const uint8_t *)bs_raw, (uint8_t *)bs_sh,
                                                                (uint32_t)N, G, gp, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_prepare_b(const void *b, int64_t N, int64_t K, void *bq_sh, void *bs_sh, bool sw, hipStream_t stream) {
+  const int G = (int)(K / 32);
+  const int gp = (G + 7) / 8 * 8;
+  const uint32_t units = (uint32_t)((N + 255) / 256 * 16) * (uint32_t)(gp / 4);
+  if (sw)
+    prepare_b_kernel<true><<<units, 64, 0, stream>>>((const uint16_t *)b, (uint8_t *)bq_sh, (uint8_t *)bs_sh, (int)N,
+                                                     (int)K, gp);
+  else
+    prepare_b_kernel<false><<<units, 64, 0, stream>>>((const uint16_t *)b, (uint8_t *)bq_sh, (uint8_t *)bs_sh, (int)N,
+                                                      (int)K, gp);
   return hipGetLastError();
 }
 

@@ -115,6 +115,22 @@ MXFP4_API mxfp4_status_t mxfp4_preshuffle_b(const void *bq, const void *bs_raw, 
                                   void *bs_shuffled, mxfp4_stream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Prepare B for mxfp4_gemm in one launch: quantize bf16 B (as               */
+/* mxfp4_quantize) and write the codes and scales straight into the layouts */
+/* mxfp4_preshuffle_b produces.  The result is byte-identical to            */
+/* mxfp4_quantize followed by mxfp4_preshuffle_b.  (Submission 608632's      */
+/* patched input generator prepares B offline: quantize, then shuffle the    */
+/* codes and the scales.)                                                    */
+/*   b_bf16      [N, K] bf16, row-major, 16-byte aligned          (input)    */
+/*   bq_shuffled [N/16, (K/2)*16] bytes, as mxfp4_preshuffle_b     (output)   */
+/*   bs_shuffled mxfp4_shuffled_scale_bytes(N, K) bytes, padding 127 (output) */
+/* Errors: INVALID_ARG (null, N < 1, K < 32, misaligned);                    */
+/*         UNSUPPORTED (N % 16 != 0, K % 32 != 0, sizes beyond 2^31 bytes). */
+/* ------------------------------------------------------------------------ */
+MXFP4_API mxfp4_status_t mxfp4_prepare_b(const void *b_bf16, int64_t N, int64_t K, void *bq_shuffled,
+                                         void *bs_shuffled, mxfp4_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* The fused GEMM: quantize A on the fly (as mxfp4_quantize), multiply by    */
 /* the preshuffled B with scaled FP4 matrix instructions, accumulate in f32, */
 /* round to bf16 (nearest even) and store C.  (submission 608632, kernel v7: */
@@ -156,6 +172,10 @@ MXFP4_API mxfp4_status_t mxfp4_reserve(int64_t M, int64_t N, int64_t K, mxfp4_st
 
 /* Human-readable name of a status code (static storage). */
 MXFP4_API const char *mxfp4_status_string(mxfp4_status_t status);
+
+/* Name of the last HIP error (hipGetErrorName) that an MXFP4_ERR_HIP result */
+/* of this thread came from, or "hipSuccess"; a static string.               */
+MXFP4_API const char *mxfp4_last_hip_error(void);
 
 /* Name of the kernel schedule mxfp4_gemm picks for a shape (thread-local
  * storage, valid until the next call on the thread), e.g.

@@ -102,6 +102,19 @@ def test_preshuffle_rejects_bad_arguments(args, code):
     assert mx.lib().mxfp4_preshuffle_b(*args, None) == code
 
 
+@pytest.mark.parametrize("args,code", [
+    ((0, 32, 64, FAKE, FAKE), INVALID),
+    ((FAKE, 0, 64, FAKE, FAKE), INVALID),
+    ((FAKE, 32, 16, FAKE, FAKE), INVALID),
+    ((FAKE + 8, 32, 64, FAKE, FAKE), INVALID),
+    ((FAKE, 24, 64, FAKE, FAKE), UNSUPPORTED),
+    ((FAKE, 32, 48, FAKE, FAKE), UNSUPPORTED),
+    ((FAKE, 1 << 16, 1 << 15, FAKE, FAKE), UNSUPPORTED),
+])
+def test_prepare_b_rejects_bad_arguments(args, code):
+    assert mx.lib().mxfp4_prepare_b(*args, None) == code
+
+
 def test_schedule_names_and_override():
     name = mx.mxfp4_gemm_schedule_name(16, 3072, 1536)
     assert re.fullmatch(r"mt\d+_nt\d+_wn\d+_wk\d+_kpw\d+_split\d+", name)

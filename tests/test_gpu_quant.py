@@ -121,3 +121,51 @@ def test_b_prep_on_gpu_equals_oracle_prep():
     qr, sr = oracle.quantize(b)
     assert np.array_equal(bw.cpu().numpy(), oracle.preshuffle_b(qr))
     assert np.array_equal(bs.cpu().numpy().reshape(-1), oracle.shuffle_scales(sr, N, K).reshape(-1))
+
+
+@pytest.mark.parametrize("N,K", [(16, 32), (32, 64), (48, 96), (288, 512), (2112, 7168), (3072, 1536), (256, 4160)])
+def test_prepare_b_equals_oracle_prep_and_two_step_prep(mode, N, K):
+    """The one-launch B preparation equals the oracle's quantize + shuffles
+    byte for byte (codes, scales and the 127 padding), and equals the
+    library's own quantize followed by preshuffle.  Some groups are scaled
+    far apart so the scales span the e8m0 range."""
+    torch = torch_cuda()
+    b = syn.normal_bf16(7 + N + K, syn.STREAM_B, (N, K))
+    b = b.copy()
+    b[0, :32] = 0  # an all-zero group
+    if N > 16 and K >= 96:
+        b[17, 64:96] = (b[17, 64:96].astype(np.uint32) + (20 << 7)).astype(np.uint16)  # x 2^20
+        b[3, 32:64] = (b[3, 32:64].astype(np.uint32) - (30 << 7)).astype(np.uint16)    # x 2^-30
+    x = to_dev_u16_as_bf16(torch, b)
+    bw, bs = mx.prepare_b(x)
+    q, s = mx.quantize(x)
+    bw2, bs2 = mx.preshuffle_b(q, s)
+    torch.cuda.synchronize()
+    qr, sr = oracle.quantize(b)
+    assert np.array_equal(bw.cpu().numpy(), oracle.preshuffle_b(qr))
+    assert np.array_equal(bs.cpu().numpy().reshape(-1), oracle.shuffle_scales(sr, N, K).reshape(-1))
+    assert np.array_equal(bw.cpu().numpy(), bw2.cpu().numpy())
+    assert np.array_equal(bs.cpu().numpy(), bs2.cpu().numpy())
+
+
+def test_library_loaded_before_torch_uses_torchs_runtime():
+    """Loading the library before anything imports torch must still leave
+    one HIP runtime in the process (torch's), and calls must work."""
+    import subprocess
+    import sys
+    from tests.conftest import ROOT
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import block_scaled_mxfp4_bf16_amd as mx\n"
+        "mx.lib()\n"
+        "import torch\n"
+        "x = torch.ones((16, 64), dtype=torch.bfloat16, device='cuda')\n"
+        "q, s = mx.quantize(x)\n"
+        "torch.cuda.synchronize()\n"
+        "assert int(q[0, 0]) == 0x66 and int(s[0, 0]) == 125, (int(q[0, 0]), int(s[0, 0]))\n"  # 1.0 / 2^-2 = 4.0: code 6
+        "maps = open('/proc/self/maps').read()\n"
+        "libs = {l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}\n"
+        "assert len(libs) == 1, libs\n"
+        "print('ok')\n" % ROOT)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr
