@@ -51,6 +51,8 @@ def _load():
         "mxfp4_prepare_b": (I, [P, I64, I64, P, P, P]),
         "mxfp4_gemm": (I, [P, P, P, P, I64, I64, I64, P]),
         "mxfp4_gemm_ex": (I, [P, P, P, P, I64, I64, I64, P, SZ, P]),
+        "mxfp4_gemm_q": (I, [P, P, P, P, P, I64, I64, I64, P]),
+        "mxfp4_gemm_q_schedule_name": (ctypes.c_char_p, [I64, I64, I64]),
         "mxfp4_reserve": (I, [I64, I64, I64, P]),
         "mxfp4_status_string": (ctypes.c_char_p, [I]),
         "mxfp4_last_hip_error": (ctypes.c_char_p, []),
@@ -74,7 +76,7 @@ def exported_symbols():
     """Names every entry point the header declares (used by the ABI test)."""
     return ["mxfp4_packed_bytes", "mxfp4_raw_scale_bytes", "mxfp4_shuffled_scale_bytes",
             "mxfp4_gemm_workspace_bytes", "mxfp4_quantize", "mxfp4_preshuffle_b", "mxfp4_prepare_b", "mxfp4_gemm",
-            "mxfp4_gemm_ex", "mxfp4_reserve", "mxfp4_status_string", "mxfp4_last_hip_error", "mxfp4_gemm_schedule_name",
+            "mxfp4_gemm_ex", "mxfp4_gemm_q", "mxfp4_gemm_q_schedule_name", "mxfp4_reserve", "mxfp4_status_string", "mxfp4_last_hip_error", "mxfp4_gemm_schedule_name",
             "mxfp4_set_quant_mode", "mxfp4_set_schedule_override"]
 
 
@@ -153,6 +155,16 @@ def mxfp4_gemm_ex(A, Bq_sh, Bs_sh, C, M: int, N: int, K: int, workspace, workspa
                                  workspace_bytes, _stream(stream)), "mxfp4_gemm_ex")
 
 
+def mxfp4_gemm_q(Aq, As, Bq_sh, Bs_sh, C, M: int, N: int, K: int, stream=None):
+    _check(_load().mxfp4_gemm_q(_ptr(Aq), _ptr(As), _ptr(Bq_sh), _ptr(Bs_sh), _ptr(C), M, N, K, _stream(stream)),
+           "mxfp4_gemm_q")
+
+
+def mxfp4_gemm_q_schedule_name(M: int, N: int, K: int):
+    r = _load().mxfp4_gemm_q_schedule_name(M, N, K)
+    return r.decode() if r is not None else None
+
+
 def mxfp4_reserve(M: int, N: int, K: int, stream=None):
     _check(_load().mxfp4_reserve(M, N, K, _stream(stream)), "mxfp4_reserve")
 
@@ -204,6 +216,16 @@ def prepare_b(b, stream=None):
     bs = bs.view(-1, ((K // 32 + 7) // 8) * 32)
     mxfp4_prepare_b(b, N, K, bw, bs, stream)
     return bw, bs
+
+
+def gemm_q(Aq, As, Bw, Bs, N: int, out=None, stream=None):
+    """C = dequant(Aq, As) * B^T as bf16 [M, N]; Aq uint8 [M, K/2], As shuffled scales."""
+    import torch
+    M, KB = Aq.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=Aq.device)
+    mxfp4_gemm_q(Aq, As, Bw, Bs, out, M, N, 2 * KB, stream)
+    return out
 
 
 def gemm(A, Bw, Bs, N: int, out=None, stream=None):

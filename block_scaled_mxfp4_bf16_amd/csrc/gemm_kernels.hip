@@ -383,6 +383,32 @@ __global__ __launch_bounds__(64) void quant_operand_kernel(const uint16_t *__res
   if ((lane & 3) == 0) blk[1024 + ch * 16 + (lane >> 2)] = (uint8_t)s;
 }
 
+// Pre-quantized A (codes [M, K/2] as mxfp4_quantize writes them, scales
+// in the shuffled layout) -> operand blocks.  One single-wave workgroup per
+// (16-row tile t, step ks): operand lane L takes the 16 code bytes of row
+// 16t + L%16, K chunk 4ks + L/16, and that group's scale byte.  Rows past M
+// and chunks past K become zero codes with scale byte 0, as quantizing
+// zeros would give.
+__global__ __launch_bounds__(64) void repack_operand_kernel(const uint8_t *__restrict__ Aq,
+                                                            const uint8_t *__restrict__ As,
+                                                            uint8_t *__restrict__ Aop, int M, int K) {
+  const int lane = threadIdx.x;
+  const int KS = (K + 127) >> 7;
+  const int t = blockIdx.x / KS, ks = blockIdx.x - (blockIdx.x / KS) * KS;
+  const int G = K >> 5, gp = (G + 7) & ~7;
+  const int row = 16 * t + (lane & 15), grp = 4 * ks + (lane >> 4);
+  const bool ok = row < M && grp < G;
+  const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Aq, 0, M * (K >> 1), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t s_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)As, 0, ((M + 255) & ~255) * gp, kRsrcWord3);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, off_or_oob(ok, row * (K >> 1) + grp * 16), 0, 0);
+  const uint32_t sc =
+      __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, off_or_oob(ok, (int)shuffled_scale_offset(row, grp, gp)), 0, 0);
+  uint8_t *blk = Aop + (size_t)(t * KS + ks) * 1088;
+  *(u32x4 *)(blk + lane * 16) = v;
+  blk[1024 + lane] = (uint8_t)sc;
+}
+
 size_t operand_a_bytes(int M, int K) { return (size_t)((M + 15) / 16) * (size_t)((K + 127) / 128) * 1088; }
 
 // ---------------------------------------------------------------- table
@@ -395,10 +421,16 @@ static hipError_t launch_variant(const GemmArgs &a, int split, bool sw, hipStrea
   const int m_tiles = (a.M + 16 * MT - 1) / (16 * MT);
   char *ws = (char *)a.workspace;
   uint8_t *aop = nullptr;
+  if (!PREQ && a.Aq) return hipErrorInvalidValue;  // pre-quantized A needs a pre-quantized schedule
   if (PREQ) {
     aop = (uint8_t *)(ws + kTicketBytes);
-    const int units = ((a.M + 15) / 16) * ((a.K + 127) / 128) * 4;
-    quant_operand_kernel<<<units, 64, 0, stream>>>((const uint16_t *)a.A, aop, a.M, a.K, units, sw ? 1 : 0);
+    if (a.Aq) {
+      const int blocks = ((a.M + 15) / 16) * ((a.K + 127) / 128);
+      repack_operand_kernel<<<blocks, 64, 0, stream>>>((const uint8_t *)a.Aq, (const uint8_t *)a.As, aop, a.M, a.K);
+    } else {
+      const int units = ((a.M + 15) / 16) * ((a.K + 127) / 128) * 4;
+      quant_operand_kernel<<<units, 64, 0, stream>>>((const uint16_t *)a.A, aop, a.M, a.K, units, sw ? 1 : 0);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

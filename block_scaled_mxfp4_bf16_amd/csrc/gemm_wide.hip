@@ -85,6 +85,38 @@ __global__ __launch_bounds__(64) void quant_quad_kernel(const uint16_t *__restri
   }
 }
 
+// Pre-quantized A (codes [M, K/2] as mxfp4_quantize writes them, scales in
+// the shuffled layout) -> quad-packed operand.  One single-wave workgroup
+// per (tile quad q, step ks): for each of the quad's four tiles, operand
+// lane L takes the 16 code bytes of row 16(4q+j) + L%16, K chunk
+// 4ks + L/16; the four tiles' scale bytes of lane L make one dword.  Rows
+// past M and chunks past K become zero codes with scale byte 0.
+__global__ __launch_bounds__(64) void repack_quad_kernel(const uint8_t *__restrict__ Aq, const uint8_t *__restrict__ As,
+                                                         uint8_t *__restrict__ Aop, int M, int K) {
+  const int lane = threadIdx.x;
+  const int KS = (K + 127) >> 7;
+  const int q = blockIdx.x / KS, ks = blockIdx.x - (blockIdx.x / KS) * KS;
+  const int G = K >> 5, gp = (G + 7) & ~7;
+  const int mq = (M + 63) >> 6;
+  const int grp = 4 * ks + (lane >> 4);
+  const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Aq, 0, M * (K >> 1), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t s_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)As, 0, ((M + 255) & ~255) * gp, kRsrcWord3);
+  u32x4 v[4];
+  uint32_t sc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (4 * q + j) * 16 + (lane & 15);
+    const bool ok = row < M && grp < G;
+    v[j] = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, off_or_oob(ok, row * (K >> 1) + grp * 16), 0, 0);
+    sc[j] = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, off_or_oob(ok, (int)shuffled_scale_offset(row, grp, gp)), 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) *(u32x4 *)(Aop + (size_t)((4 * q + j) * KS + ks) * 1024 + lane * 16) = v[j];
+  uint32_t *scales = (uint32_t *)(Aop + (size_t)mq * 4 * KS * 1024);
+  scales[(size_t)(q * KS + ks) * 64 + lane] = sc[0] | (sc[1] << 8) | (sc[2] << 16) | (sc[3] << 24);
+}
+
 // Scaled FP4 x FP4 matrix instruction whose A scale is byte `sel` of the
 // scale dword (the instruction's byte select must be a constant; `sel` is
 // one after unrolling).
@@ -364,7 +396,10 @@ static hipError_t launch_wide(const GemmArgs &a, int split, bool sw, hipStream_t
   char *ws = (char *)a.workspace;
   uint8_t *aop = (uint8_t *)(ws + kTicketBytes);
   const int units = ((a.M + 63) / 64) * ((a.K + 127) / 128);
-  quant_quad_kernel<<<units, 64, 0, stream>>>((const uint16_t *)a.A, aop, a.M, a.K, units, sw ? 1 : 0);
+  if (a.Aq)
+    repack_quad_kernel<<<units, 64, 0, stream>>>((const uint8_t *)a.Aq, (const uint8_t *)a.As, aop, a.M, a.K);
+  else
+    quant_quad_kernel<<<units, 64, 0, stream>>>((const uint16_t *)a.A, aop, a.M, a.K, units, sw ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_tiles = a.N / (16 * NW);

@@ -70,11 +70,13 @@ const Tuned kTuned[] = {
     {256, 7168, 7168, "wide_mt4_nt7_w4_d2_split1"},
 };
 
-bool pick_schedule(int M, int N, int K, Schedule *out) {
+// need_pq: only schedules that read a pre-quantized A operand (for A that
+// arrives quantized).
+bool pick_schedule(int M, int N, int K, Schedule *out, bool need_pq = false) {
   for (const Tuned &t : kTuned)
     if (t.M == M && t.N == N && t.K == K) {
       Schedule s;
-      if (parse_name(t.name, &s) && covers(s, M, N, K)) {
+      if (parse_name(t.name, &s) && covers(s, M, N, K) && (s.pq || !need_pq)) {
         *out = s;
         return true;
       }
@@ -120,7 +122,8 @@ bool pick_schedule(int M, int N, int K, Schedule *out) {
   for (int v = 0; v < num_gemm_variants(); ++v) {
     Schedule s;
     gemm_variant_shape(v, &s);
-    if (s.mt != mt || s.pq || s.wide || (s.rb == 8) != (M <= 8)) continue;
+    if (s.mt != mt || s.pq != (need_pq ? 1 : 0) || s.wide) continue;
+    if (!need_pq && (s.rb == 8) != (M <= 8)) continue;
     for (s.split = 1; s.split <= 16; ++s.split) {
       if (!covers(s, M, N, K)) continue;
       const int per_wg = (ks + s.split - 1) / s.split;
@@ -180,12 +183,22 @@ bool parse_schedule(const std::string &name, int M, int N, int K, Schedule *out)
   return true;
 }
 
-bool choose(int M, int N, int K, Schedule *s) {
+// The name mxfp4_set_schedule_override accepts for a schedule.
+void schedule_to_name(const Schedule &s, char *buf, size_t n) {
+  if (s.wide)
+    snprintf(buf, n, "wide_mt%d_nt%d_w%d_d%d_split%d", s.mt, s.nt, s.wk, s.kpw, s.split);
+  else
+    snprintf(buf, n, "mt%d_nt%d_wn%d_wk%d_kpw%d_split%d%s", s.mt, s.nt, s.wn, s.wk, s.kpw, s.split,
+             s.pq ? "_pq" : (s.rb == 8 ? "_r8" : ""));
+}
+
+bool choose(int M, int N, int K, Schedule *s, bool need_pq = false) {
   {
     std::lock_guard<std::mutex> lk(g_opt_mu);
-    if (g_schedule_override_set) return parse_schedule(g_schedule_override, M, N, K, s);
+    if (g_schedule_override_set)
+      return parse_schedule(g_schedule_override, M, N, K, s) && (s->pq || !need_pq);
   }
-  return pick_schedule(M, N, K, s);
+  return pick_schedule(M, N, K, s, need_pq);
 }
 
 mxfp4_status_t check_gemm_args(const void *A, const void *Bq, const void *Bs, const void *C, int64_t M, int64_t N,
@@ -290,11 +303,7 @@ const char *mxfp4_gemm_schedule_name(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 1 || K % 64 != 0 || N % 32 != 0) return nullptr;
   Schedule s;
   if (!choose((int)M, (int)N, (int)K, &s)) return nullptr;
-  if (s.wide)
-    snprintf(buf, sizeof(buf), "wide_mt%d_nt%d_w%d_d%d_split%d", s.mt, s.nt, s.wk, s.kpw, s.split);
-  else
-    snprintf(buf, sizeof(buf), "mt%d_nt%d_wn%d_wk%d_kpw%d_split%d%s", s.mt, s.nt, s.wn, s.wk, s.kpw, s.split,
-             s.pq ? "_pq" : (s.rb == 8 ? "_r8" : ""));
+  schedule_to_name(s, buf, sizeof(buf));
   return buf;
 }
 
@@ -377,6 +386,32 @@ mxfp4_status_t mxfp4_gemm(const void *A, const void *Bq_sh, const void *Bs_sh, v
   if (st != MXFP4_OK) return st;
   GemmArgs a{A, Bq_sh, Bs_sh, C, ws, (int)M, (int)N, (int)K};
   return hip_status(launch_gemm(s, a, sw_quant(), (hipStream_t)stream));
+}
+
+mxfp4_status_t mxfp4_gemm_q(const void *Aq, const void *As_shuffled, const void *Bq_sh, const void *Bs_sh, void *C,
+                            int64_t M, int64_t N, int64_t K, mxfp4_stream_t stream) {
+  if (!As_shuffled) return MXFP4_ERR_INVALID_ARG;
+  mxfp4_status_t st = check_gemm_args(Aq, Bq_sh, Bs_sh, C, M, N, K);
+  if (st != MXFP4_OK) return st;
+  if (pad_to(M, 256) * pad_to(K / 32, 8) >= kMaxBytes) return MXFP4_ERR_UNSUPPORTED;
+  Schedule s;
+  if (!choose((int)M, (int)N, (int)K, &s, true)) return MXFP4_ERR_UNSUPPORTED;
+  void *ws = nullptr;
+  st = get_workspace(gemm_workspace_bytes(s, (int)M, (int)N, (int)K), (hipStream_t)stream, &ws);
+  if (st != MXFP4_OK) return st;
+  GemmArgs a{nullptr, Bq_sh, Bs_sh, C, ws, (int)M, (int)N, (int)K};
+  a.Aq = Aq;
+  a.As = As_shuffled;
+  return hip_status(launch_gemm(s, a, false, (hipStream_t)stream));
+}
+
+const char *mxfp4_gemm_q_schedule_name(int64_t M, int64_t N, int64_t K) {
+  static thread_local char buf[96];
+  if (M < 1 || N < 1 || K < 64 || K % 64 != 0 || N % 32 != 0) return nullptr;
+  Schedule s;
+  if (!choose((int)M, (int)N, (int)K, &s, true)) return nullptr;
+  schedule_to_name(s, buf, sizeof(buf));
+  return buf;
 }
 
 mxfp4_status_t mxfp4_reserve(int64_t M, int64_t N, int64_t K, mxfp4_stream_t stream) {

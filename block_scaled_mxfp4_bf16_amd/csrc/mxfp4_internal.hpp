@@ -41,6 +41,10 @@ struct GemmArgs {
   void *C;
   void *workspace;
   int M, N, K;
+  // A already quantized (mxfp4_gemm_q): codes [M, K/2] and shuffled scales;
+  // then A is unused and only pre-quantized schedules run.
+  const void *Aq = nullptr;
+  const void *As = nullptr;
 };
 
 // Kernel table queries (gemm_kernels.hip).

@@ -131,6 +131,26 @@ MXFP4_API mxfp4_status_t mxfp4_prepare_b(const void *b_bf16, int64_t N, int64_t 
                                          void *bs_shuffled, mxfp4_stream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* The GEMM with A already quantized: C = dequant(Aq, As) * B^T, bf16 out.   */
+/* A quantized once can serve several GEMMs.  (Submission 711914 quantizes   */
+/* A with a standalone kernel and hands FP4 A and its shuffled scales to the */
+/* GEMM for large M; mxfp4_quantize with shuffled_scales = 1 writes exactly  */
+/* these inputs.)  Same C as mxfp4_gemm on the bf16 A when both run the same */
+/* pre-quantized schedule; only such schedules run here.                     */
+/*   Aq      [M, K/2] packed e2m1, natural layout, 16-byte aligned (input)   */
+/*   As      shuffled scales, mxfp4_shuffled_scale_bytes(M, K) bytes (input) */
+/*   Bq_sh, Bs_sh, C, M, N, K, stream: as mxfp4_gemm                         */
+/* Uses the library-owned workspace of (device, stream), like mxfp4_gemm.    */
+/* Errors: as mxfp4_gemm; INVALID_ARG also for a null As.                    */
+/* ------------------------------------------------------------------------ */
+MXFP4_API mxfp4_status_t mxfp4_gemm_q(const void *Aq, const void *As, const void *Bq_sh, const void *Bs_sh, void *C,
+                                      int64_t M, int64_t N, int64_t K, mxfp4_stream_t stream);
+
+/* Name of the schedule mxfp4_gemm_q would run for a shape (a pre-quantized  */
+/* one), or NULL if none covers it.  Thread-local static string.            */
+MXFP4_API const char *mxfp4_gemm_q_schedule_name(int64_t M, int64_t N, int64_t K);
+
+/* ------------------------------------------------------------------------ */
 /* The fused GEMM: quantize A on the fly (as mxfp4_quantize), multiply by    */
 /* the preshuffled B with scaled FP4 matrix instructions, accumulate in f32, */
 /* round to bf16 (nearest even) and store C.  (submission 608632, kernel v7: */

@@ -115,6 +115,23 @@ def test_prepare_b_rejects_bad_arguments(args, code):
     assert mx.lib().mxfp4_prepare_b(*args, None) == code
 
 
+def test_gemm_q_rejects_bad_arguments_and_names_pre_quantized_schedules():
+    L = mx.lib()
+    assert L.mxfp4_gemm_q(FAKE, None, FAKE, FAKE, FAKE, 16, 64, 128, None) == INVALID
+    assert L.mxfp4_gemm_q(None, FAKE, FAKE, FAKE, FAKE, 16, 64, 128, None) == INVALID
+    assert L.mxfp4_gemm_q(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 64, 96, None) == UNSUPPORTED
+    assert L.mxfp4_gemm_q(FAKE + 8, FAKE, FAKE, FAKE, FAKE, 16, 64, 128, None) == INVALID
+    for shape in ((1, 64, 128), (8, 2112, 7168), (16, 3072, 1536), (32, 4096, 512), (64, 7168, 2048)):
+        assert mx.mxfp4_gemm_q_schedule_name(*shape).endswith("_pq"), shape
+    assert mx.mxfp4_gemm_q_schedule_name(256, 7168, 7168).startswith("wide_")
+    # an override that reads bf16 A cannot serve pre-quantized A
+    mx.mxfp4_set_schedule_override("mt1_nt1_wn2_wk4_kpw1_split3")
+    try:
+        assert mx.mxfp4_gemm_q_schedule_name(16, 3072, 1536) is None
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+
+
 def test_schedule_names_and_override():
     name = mx.mxfp4_gemm_schedule_name(16, 3072, 1536)
     assert re.fullmatch(r"mt\d+_nt\d+_wn\d+_wk\d+_kpw\d+_split\d+", name)
@@ -171,6 +188,7 @@ def test_every_schedule_the_gpu_tests_name_covers_its_shape():
     cases = [(s, M, N, K) for s, M, N, K in g.WIDE_CASES]
     cases += [(s, M, 256, 2048 + 64) for s in g.R8_SCHEDULES for M in (1, 5, 8)]
     cases += [(s, 70, 224, 1088) for s in ("wide_mt4_nt7_w4_d2_split1", "wide_mt8_nt2_w8_d2_split2")]
+    cases += [(s, M, N, K) for s, M, N, K in g.GEMM_Q_CASES]
     try:
         for s in g.SCHEDULES:  # compiled (the test skips those that cannot cover its K)
             mx.mxfp4_set_schedule_override(s)

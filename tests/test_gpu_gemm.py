@@ -256,3 +256,45 @@ def test_wide_kernel_matches_oracle(sched, M, N, K):
         mx.mxfp4_set_schedule_override(None)
     assert np.array_equal(first, second)
     assert_close(first, c.ref(), "%s %dx%dx%d" % (sched, M, N, K))
+
+
+# A quantized once, handed to the GEMM: (schedule or None for the default, M, N, K)
+GEMM_Q_CASES = [("mt4_nt1_wn2_wk4_kpw4_split1_pq", 64, 7168, 2048), ("mt1_nt1_wn1_wk8_kpw4_split2_pq", 8, 2112, 7168),
+                ("mt2_nt1_wn1_wk1_kpw4_split1_pq", 32, 4096, 512), ("mt4_nt2_wn2_wk2_kpw4_split3_pq", 40, 256, 2112),
+                ("wide_mt4_nt7_w4_d2_split1", 130, 224, 1088), ("wide_mt8_nt2_w8_d2_split2", 200, 128, 1600),
+                ("wide_mt4_nt1_w8_d4_split3", 65, 96, 448)]
+
+
+@pytest.mark.parametrize("sched,M,N,K", GEMM_Q_CASES)
+def test_gemm_q_equals_gemm_under_the_same_schedule(sched, M, N, K):
+    """Quantizing A with mxfp4_quantize and calling mxfp4_gemm_q gives the
+    same bits as mxfp4_gemm on the bf16 A under the same schedule: the
+    operand bytes are identical and so is the arithmetic."""
+    torch = torch_cuda()
+    c = make(torch, M, N, K, seed=3 * M + N + K)
+    aq, as_ = mx.quantize(c.A, shuffled_scales=True)
+    mx.mxfp4_set_schedule_override(sched)
+    try:
+        assert mx.mxfp4_gemm_q_schedule_name(M, N, K) == sched
+        cq = bf16_dev_to_bits(mx.gemm_q(aq, as_, c.Bw, c.Bs, N))
+        cf = c.run()
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+    assert np.array_equal(cq, cf)
+    assert_close(cq, c.ref(), sched)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_gemm_q_default_schedule_on_oracle_quantized_a(name):
+    """mxfp4_gemm_q fed the oracle's own quantized A (codes and shuffled
+    scales) under its default schedule matches the oracle's product."""
+    torch = torch_cuda()
+    w = syn.CONFIGS[name]
+    c = Case(torch, w.a_bits(), w.b_bits())
+    qa, sa = oracle.quantize(c.a_bits)
+    aq = to_dev_u8(torch, qa)
+    as_ = to_dev_u8(torch, oracle.shuffle_scales(sa, c.M, c.K))
+    assert mx.mxfp4_gemm_q_schedule_name(c.M, c.N, c.K).endswith("_pq")
+    got = bf16_dev_to_bits(mx.gemm_q(aq, as_, c.Bw, c.Bs, c.N))
+    torch.cuda.synchronize()
+    assert_close(got, c.ref(), name)
