@@ -36,10 +36,11 @@ std::mutex g_opt_mu;
 std::string g_schedule_override;
 bool g_schedule_override_set = false;
 
-// Schedule choice: search the compiled kernel table.  The workgroup covers
-// all of M when M <= 64 (so every B byte is fetched once); among the kernels
-// that can cover K, prefer 256-2048 workgroups, then the fewest K splits
-// across workgroups, then the least idle work per wave.
+// Schedule choice: the tuned table for the shapes measured on MI355X;
+// otherwise, for M <= 64, a search of the compiled fused kernels with
+// 16-row tiles that prefers 256-2048 workgroups, then the fewest K splits
+// across workgroups, then the least idle work per wave; for M > 64, the
+// large-M kernel whose workgroups take in the fewest bytes.
 int tiles_of(const Schedule &s, int M, int N) {
   return (N / (16 * s.nt * s.wn)) * ((M + 16 * s.mt - 1) / (16 * s.mt));
 }
@@ -64,10 +65,15 @@ struct Tuned {
 };
 const Tuned kTuned[] = {
     {16, 3072, 1536, "mt1_nt2_wn1_wk8_kpw2_split1"},
-    {32, 4096, 512, "mt2_nt2_wn1_wk4_kpw1_split1"},
+    {32, 4096, 512, "mt1_nt1_wn4_wk1_kpw4_split1"},
     {8, 2112, 7168, "mt1_nt2_wn1_wk8_kpw4_split2_r8"},
-    {64, 7168, 2048, "mt4_nt1_wn2_wk4_kpw4_split1_pq"},
+    {64, 7168, 2048, "mt1_nt2_wn4_wk4_kpw4_split1"},
     {256, 7168, 7168, "wide_mt4_nt7_w4_d2_split1"},
+    // the leaderboard's other shapes
+    {4, 2880, 512, "mt1_nt1_wn1_wk4_kpw1_split1_r8"},
+    {16, 2112, 7168, "mt1_nt1_wn4_wk4_kpw4_split4"},
+    {32, 2880, 512, "mt1_nt1_wn4_wk1_kpw4_split1"},
+    {256, 3072, 1536, "mt1_nt1_wn4_wk4_kpw4_split1"},
 };
 
 // need_pq: only schedules that read a pre-quantized A operand (for A that
@@ -114,7 +120,10 @@ bool pick_schedule(int M, int N, int K, Schedule *out, bool need_pq = false) {
       return true;
     }
   }
-  const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  // 16-row tiles: each workgroup then stages a quarter to a half as much A
+  // as a 32- or 64-row tile would, and there are more workgroups to spread
+  // B over; measured best at M = 32 and 64 as well as at M = 16
+  const int mt = 1;
   const int ks = (K + 127) / 128;
   bool found = false;
   Schedule best{};
