@@ -28,6 +28,8 @@
 //           tiles 4q..4q+3 (byte j for tile 4q+j).
 // One dword per lane then serves the scale operand of four matrix
 // instructions, selected by the instruction's operand byte select.
+#include <type_traits>
+
 #include "mxfp4_device.hpp"
 #include "mxfp4_internal.hpp"
 
@@ -38,13 +40,14 @@ size_t quad_operand_bytes(int M, int K) {
   return mq * ks * (4 * 1024 + 256);
 }
 
-// One single-wave workgroup per (tile quad, K step): 64 rows x 128
-// elements of bf16 A, in sixteen coalesced 16-byte loads per lane (each
-// covers 16 rows x one 32-element group, four lanes per group, as in the
-// fused kernels' staging).  One wave per workgroup spreads the units over
-// as many CUs as there are units: each CU's intake from HBM, not the
-// arithmetic, is what bounds this kernel.  Rows past M and chunks past K
-// load as zeros and are written as zero codes with scale byte 0.
+// One single-wave workgroup per (16-row tile, K step): 16 rows x 128
+// elements of bf16 A, in four coalesced 16-byte loads per lane (each covers
+// the 16 rows x one 32-element group, four lanes per group, as in the fused
+// kernels' staging).  Small units spread the work over many CUs: each CU's
+// intake from HBM, not the arithmetic, bounds this kernel.  The tile's
+// scale bytes go to byte j = t % 4 of the quad's scale dwords.  Rows past M
+// and chunks past K load as zeros and are written as zero codes with scale
+// byte 0; the tiles of the last quad past M are written the same way.
 __global__ __launch_bounds__(64) void quant_quad_kernel(const uint16_t *__restrict__ A, uint8_t *__restrict__ Aop,
                                                         int M, int K, int units, int sw_quant) {
   const int lane = threadIdx.x;
@@ -52,37 +55,35 @@ __global__ __launch_bounds__(64) void quant_quad_kernel(const uint16_t *__restri
   if (unit >= units) return;
   const int KS = (K + 127) >> 7;
   const int ks = unit % KS;
-  const int q = unit / KS;
+  const int t = unit / KS;  // 16-row tile
   const int mq = (M + 63) >> 6;
   const int a_bytes = M * K * 2;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, a_bytes, kRsrcWord3);
-  u32x4 w[4][4];
+  u32x4 w[4];
+  const int row = t * 16 + (lane >> 2);
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-      const int row = (4 * q + j) * 16 + (lane >> 2);
-      const int kel = ks * 128 + ch * 32 + (lane & 3) * 8;
-      const bool ok = (row < M) && (ks * 128 + ch * 32 < K);
-      w[j][ch] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ok ? (row * K + kel) * 2 : a_bytes, 0, 0);
-    }
+  for (int ch = 0; ch < 4; ++ch) {
+    const int kel = ks * 128 + ch * 32 + (lane & 3) * 8;
+    const bool ok = (row < M) && (ks * 128 + ch * 32 < K);
+    w[ch] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off_or_oob(ok, (row * K + kel) * 2), 0, 0);
+  }
   uint32_t *codes = (uint32_t *)Aop;
-  uint32_t *scales = (uint32_t *)(Aop + (size_t)mq * 4 * KS * 1024);
-  uint32_t sc[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
+  uint8_t *scales = Aop + (size_t)mq * 4 * KS * 1024;
+  auto run = [&](auto sw_tag) {
+    constexpr bool SW = decltype(sw_tag)::value;
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
       uint32_t s;
-      const uint32_t d = quant_quarter(w[j][ch], sw_quant, &s);
+      const uint32_t d = quant_quarter_t<SW>(w[ch], &s);
       // lane = 4*row + quarter: dword (16*ch + row)*4 + quarter of the block
-      codes[(size_t)((4 * q + j) * KS + ks) * 256 + ch * 64 + lane] = d;
-      sc[ch] |= s << (8 * j);
+      codes[(size_t)(t * KS + ks) * 256 + ch * 64 + lane] = d;
+      if ((lane & 3) == 0) scales[((size_t)((t >> 2) * KS + ks) * 64 + ch * 16 + (lane >> 2)) * 4 + (t & 3)] = (uint8_t)s;
     }
-  if ((lane & 3) == 0) {
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) scales[(size_t)(q * KS + ks) * 64 + ch * 16 + (lane >> 2)] = sc[ch];
-  }
+  };
+  if (sw_quant)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 }
 
 // Pre-quantized A (codes [M, K/2] as mxfp4_quantize writes them, scales in
@@ -399,7 +400,7 @@ static hipError_t launch_wide(const GemmArgs &a, int split, bool sw, hipStream_t
   if (a.Aq)
     repack_quad_kernel<<<units, 64, 0, stream>>>((const uint8_t *)a.Aq, (const uint8_t *)a.As, aop, a.M, a.K);
   else
-    quant_quad_kernel<<<units, 64, 0, stream>>>((const uint16_t *)a.A, aop, a.M, a.K, units, sw ? 1 : 0);
+    quant_quad_kernel<<<units * 4, 64, 0, stream>>>((const uint16_t *)a.A, aop, a.M, a.K, units * 4, sw ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_tiles = a.N / (16 * NW);
