@@ -298,3 +298,26 @@ def test_gemm_q_default_schedule_on_oracle_quantized_a(name):
     got = bf16_dev_to_bits(mx.gemm_q(aq, as_, c.Bw, c.Bs, c.N))
     torch.cuda.synchronize()
     assert_close(got, c.ref(), name)
+
+
+# Shapes outside the tuned table: the default schedule choice for small,
+# ragged and large M, long and half-step K, narrow and odd-tile N.
+DEFAULT_SHAPES = [(1, 32, 64), (3, 96, 4160), (17, 288, 448), (48, 1024, 1024), (65, 96, 192), (100, 224, 2112),
+                  (300, 64, 1088), (513, 288, 640), (64, 32, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", DEFAULT_SHAPES)
+def test_default_schedules_match_oracle(M, N, K):
+    torch = torch_cuda()
+    c = make(torch, M, N, K, seed=5 * M + 3 * N + K)
+    ref = c.ref()
+    assert_close(c.run(), ref, "gemm %dx%dx%d (%s)" % (M, N, K, mx.mxfp4_gemm_schedule_name(M, N, K)))
+    aq, as_ = mx.quantize(c.A, shuffled_scales=True)
+    got_q = bf16_dev_to_bits(mx.gemm_q(aq, as_, c.Bw, c.Bs, N))
+    assert_close(got_q, ref, "gemm_q %dx%dx%d (%s)" % (M, N, K, mx.mxfp4_gemm_q_schedule_name(M, N, K)))
+    need = mx.mxfp4_gemm_workspace_bytes(M, N, K)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    mx.mxfp4_gemm_ex(c.A, c.Bw, c.Bs, C, M, N, K, ws if need else None, need)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_dev_to_bits(C), c.run())
