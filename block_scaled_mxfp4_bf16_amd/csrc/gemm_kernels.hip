@@ -458,9 +458,11 @@ struct Variant {
 // large-M kernels: W waves split K; listed with wn = 1, wk = W, kpw = the
 // number of steps loaded ahead
 #define VW(MW, NW, W, D) {MW, NW, 1, W, D, 1, launch_wide_##MW##_##NW##_##W##_##D, 16, 1},
+#define VWL(MW, NW, W, D) {MW, NW, 1, W, D, 1, launch_widel_##MW##_##NW##_##W##_##D, 16, 3},
 
 static const Variant kVariants[] = {
     MXFP4_WIDE_VARIANTS(VW)
+    MXFP4_WIDEL_VARIANTS(VWL)
     V8(1, 1, 1, 16, 4), V8(1, 1, 1, 14, 4), V8(1, 1, 1, 8, 4), V8(1, 1, 1, 16, 2), V8(1, 1, 2, 8, 4), V8(1, 1, 2, 8, 2),
     V8(1, 2, 1, 16, 4), V8(1, 2, 1, 8, 4), V8(1, 1, 1, 4, 4), V8(1, 1, 1, 4, 2), V8(1, 1, 1, 8, 2), V8(1, 1, 1, 4, 1),
     V8(1, 1, 2, 4, 2), V8(1, 1, 4, 4, 4), V8(1, 1, 1, 2, 2), V8(1, 1, 1, 1, 4), V8(1, 1, 1, 2, 4),
@@ -518,6 +520,7 @@ static const Variant kVariants[] = {
 
 #undef V
 #undef VW
+#undef VWL
 #undef V8
 #undef VQ
 

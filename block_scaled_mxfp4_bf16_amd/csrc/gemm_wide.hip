@@ -142,7 +142,19 @@ __device__ __forceinline__ int uniform_off(bool in_range, int off) {
 // 16*NW columns, K steps [S0, S1) of its split; wave w takes steps S0 + w,
 // S0 + w + W, ...  Each wave keeps the whole tile's accumulators in
 // registers and D steps of operands in flight.
-template <int MW, int NW, int W, int D>
+// BL: B's codes go straight from memory into a per-wave LDS ring of D
+// slots (one step's NW operand blocks each) instead of registers, so the
+// registers that would have held them hold deeper A stages; each lane reads
+// back exactly the 16 bytes it loaded, right before the step's MFMAs.
+// s_waitcnt for vmcnt <= N, expcnt and lgkmcnt left alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int MW, int NW, int W, int D, bool BL>
 __global__ __launch_bounds__(64 * W) void gemm_wide_kernel(const uint8_t *__restrict__ Aop,
                                                           const uint8_t *__restrict__ Bw,
                                                           const uint8_t *__restrict__ Bs, uint16_t *__restrict__ C,
@@ -156,8 +168,17 @@ __global__ __launch_bounds__(64 * W) void gemm_wide_kernel(const uint8_t *__rest
   constexpr int NSD = (NW + 1) / 2;  // B scale dwords per step: 32-row blocks the NW subtiles touch
   constexpr int E = MW * NW * 256;   // outputs per tile
   constexpr int RS = 4;              // partial tiles LDS holds at once
-  static_assert(RS * E * 4 <= 160 * 1024 - 64, "partial tiles must fit in LDS");
-  __shared__ __attribute__((aligned(16))) float red[RS * E];
+  // the B ring and the partial tiles share one LDS array
+  constexpr int kRedBytes = RS * E * 4;
+  // per wave: a 1 KiB block the first DMA load lands in, then D slots of NW
+  // operand blocks
+  constexpr int kWaveRing = (D * NW + 1) * 1024;
+  constexpr int kRingBytes = BL ? W * kWaveRing : 0;
+  constexpr int kLdsBytes = kRedBytes > kRingBytes ? kRedBytes : kRingBytes;
+  static_assert(kLdsBytes <= 160 * 1024 - 64, "partial tiles and B ring must fit in LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  float *const red = (float *)lds;
+  uint8_t *const ring = lds;
   __shared__ uint32_t s_last;
 
   const int lane = threadIdx.x & 63;
@@ -205,12 +226,26 @@ __global__ __launch_bounds__(64 * W) void gemm_wide_kernel(const uint8_t *__rest
   struct Stage {
     u32x4 a[MW];
     uint32_t as[MQ];
-    u32x4 b[NW];
+    u32x4 b[BL ? 1 : NW];
     uint32_t bs[NSD];
   };
-  auto load = [&](int ks, Stage &st) {
+  // Byte offset of a ring slot: this wave's slot d, operand block nt.
+  auto ring_at = [&](int d, int nt) { return wave * kWaveRing + (1 + d * NW + nt) * 1024; };
+  auto load = [&](int ks, Stage &st, int d) {
     const bool ok = ks < S1;
     const int lb = ks == KS - 1 ? l16b : l16;
+    if constexpr (BL) {
+      // B first: the step's A (in registers) arrives after it, so waiting
+      // for A also covers the ring slot
+#pragma unroll
+      for (int nt = 0; nt < NW; ++nt)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (__attribute__((address_space(3))) void *)(ring + ring_at(d, nt)),
+                                                 16, uniform_off(ok, (gw + nt) * K * 8 + ks * 1024) + lb, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < NSD; ++q)
+        st.bs[q] = __builtin_amdgcn_raw_buffer_load_b32(
+            s_rsrc, uniform_off(ok, ((gw >> 1) + q) * gp * 32 + (ks >> 1) * 256) + l4, 0, 0);
+    }
 #pragma unroll
     for (int mw = 0; mw < MW; ++mw)
       st.a[mw] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, uniform_off(ok, ((t0 + mw) * KS + ks) * 1024) + l16, 0, 0);
@@ -218,14 +253,24 @@ __global__ __launch_bounds__(64 * W) void gemm_wide_kernel(const uint8_t *__rest
     for (int q = 0; q < MQ; ++q)
       st.as[q] = __builtin_amdgcn_raw_buffer_load_b32(
           as_rsrc, uniform_off(ok, ((m_tile * MQ + q) * KS + ks) * 256) + l4, 0, 0);
+    if constexpr (!BL) {
 #pragma unroll
-    for (int nt = 0; nt < NW; ++nt)
-      st.b[nt] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, uniform_off(ok, (gw + nt) * K * 8 + ks * 1024) + lb, 0, 0);
+      for (int nt = 0; nt < NW; ++nt)
+        st.b[nt] =
+            __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, uniform_off(ok, (gw + nt) * K * 8 + ks * 1024) + lb, 0, 0);
 #pragma unroll
-    for (int d = 0; d < NSD; ++d)
-      st.bs[d] = __builtin_amdgcn_raw_buffer_load_b32(
-          s_rsrc, uniform_off(ok, ((gw >> 1) + d) * gp * 32 + (ks >> 1) * 256) + l4, 0, 0);
+      for (int q = 0; q < NSD; ++q)
+        st.bs[q] = __builtin_amdgcn_raw_buffer_load_b32(
+            s_rsrc, uniform_off(ok, ((gw >> 1) + q) * gp * 32 + (ks >> 1) * 256) + l4, 0, 0);
+    }
   };
+  // Loads per stage, and how many are issued after a stage's B by the time
+  // its slot is read in the steady loop: its own scales and A, and the
+  // D - 1 other stages.
+  constexpr int kLoadsPerStage = NW + NSD + MW + MQ;
+  constexpr int kOwnAfterB = NSD + MW + MQ;
+  constexpr int kAfterB = (D - 1) * kLoadsPerStage + kOwnAfterB;
+  static_assert(!BL || kAfterB <= 63, "the load counter holds at most 63");
 
   // The scale byte of B subtile nt: the dword of its 32-row block, byte
   // (row block half) | 2 * (step parity); a wave's steps all share a parity
@@ -242,7 +287,26 @@ __global__ __launch_bounds__(64 * W) void gemm_wide_kernel(const uint8_t *__rest
 #pragma unroll
     for (int nt = 0; nt < NW; ++nt) acc[mw][nt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Stage &st) {
+  // B operand blocks of ring slot d, read back once the slot's loads have
+  // landed.  The slot is written by the memory system, not by an
+  // instruction the compiler tracks, so the wait is explicit: `after` loads
+  // issued after the slot's B may still be outstanding.
+  // `later` stages (0 .. D-1) issued their loads after slot d's.
+  auto ring_read = [&](int d, int later, u32x4 (&bl)[NW]) {
+    if constexpr (BL) {
+      switch (later) {
+        case 0: wait_vmcnt<kOwnAfterB>(); break;
+        case 1: wait_vmcnt<kOwnAfterB + (D > 1 ? kLoadsPerStage : 0)>(); break;
+        case 2: wait_vmcnt<kOwnAfterB + (D > 2 ? 2 * kLoadsPerStage : 0)>(); break;
+        default: wait_vmcnt<kAfterB>(); break;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nt = 0; nt < NW; ++nt) bl[nt] = *(const u32x4 *)(ring + ring_at(d, nt) + l16);
+    }
+  };
+  auto compute = [&](const Stage &st, const u32x4 (&bl)[NW]) {
+    const u32x4 *bv = BL ? bl : st.b;
     uint32_t sb[NW];
 #pragma unroll
     for (int nt = 0; nt < NW; ++nt) {
@@ -254,7 +318,7 @@ __global__ __launch_bounds__(64 * W) void gemm_wide_kernel(const uint8_t *__rest
       const v8i a_op = {(int)st.a[mw].x, (int)st.a[mw].y, (int)st.a[mw].z, (int)st.a[mw].w, 0, 0, 0, 0};
 #pragma unroll
       for (int nt = 0; nt < NW; ++nt) {
-        const v8i b_op = {(int)st.b[nt].x, (int)st.b[nt].y, (int)st.b[nt].z, (int)st.b[nt].w, 0, 0, 0, 0};
+        const v8i b_op = {(int)bv[nt].x, (int)bv[nt].y, (int)bv[nt].z, (int)bv[nt].w, 0, 0, 0, 0};
         acc[mw][nt] = mfma_fp4_sel(a_op, b_op, acc[mw][nt], mw & 3, st.as[mw >> 2], sb[nt]);
       }
     }
@@ -267,26 +331,52 @@ __global__ __launch_bounds__(64 * W) void gemm_wide_kernel(const uint8_t *__rest
   // a load or a use makes the compiler wait for every load in flight where
   // the paths meet); steps past the run load zeros and add nothing, and the
   // last round issues no loads.
+  // With BL the loop is rotated so that each stage reads the next slot
+  // after issuing its own reload: a ring read at the top of the loop would
+  // follow the previous iteration's last ring load across the back edge,
+  // where the compiler can no longer tell the slots apart and waits for it.
+  if constexpr (BL) {
+    // The compiler checks an LDS read against the first LDS-DMA load of the
+    // array it meets and, unless their addresses differ by a constant that
+    // keeps them apart, waits for every DMA load in flight.  Make that first
+    // load one out of range (it fetches nothing and writes zeros) into this
+    // wave's block below its ring, which no read touches; the ring reads
+    // carry their own exact waits.
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        b_rsrc, (__attribute__((address_space(3))) void *)(ring + wave * kWaveRing), 16, (int)0x80000000u, 0, 0, 0);
+  }
   Stage st[D];
+  u32x4 bl[NW];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    load(ks0 + W * d, st[d]);
+    load(ks0 + W * d, st[d], d);
     __builtin_amdgcn_sched_barrier(0);
   }
   const int nsteps = ks0 < S1 ? (S1 - ks0 + W - 1) / W : 0;
   const int rounds = (nsteps + D - 1) / D;
+  if (rounds > 0) ring_read(0, D - 1, bl);
   for (int it = 0; it + 1 < rounds; ++it) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      compute(st[d]);
+      compute(st[d], bl);
       __builtin_amdgcn_sched_barrier(0);
-      load(ks0 + W * ((it + 1) * D + d), st[d]);
+      load(ks0 + W * ((it + 1) * D + d), st[d], d);
       __builtin_amdgcn_sched_barrier(0);
+      ring_read((d + 1) % D, D - 1, bl);
     }
   }
   if (rounds > 0) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) compute(st[d]);
+    for (int d = 0; d < D; ++d) {
+      compute(st[d], bl);
+      // last round: no reloads, so fewer loads follow each slot's B
+      if (d + 1 < D) ring_read(d + 1, D - 2 - d, bl);
+    }
+  }
+  if constexpr (BL) {
+    // the partial tiles reuse the ring: every wave's loads must have landed
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
   // Add the waves' tiles through LDS, four at a time.  Element index e =
@@ -392,7 +482,7 @@ __global__ __launch_bounds__(64 * W) void gemm_wide_kernel(const uint8_t *__rest
   if (threadIdx.x == 0) __hip_atomic_store(&tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MW, int NW, int W, int D>
+template <int MW, int NW, int W, int D, bool BL>
 static hipError_t launch_wide(const GemmArgs &a, int split, bool sw, hipStream_t stream) {
   char *ws = (char *)a.workspace;
   uint8_t *aop = (uint8_t *)(ws + kTicketBytes);
@@ -409,7 +499,7 @@ static hipError_t launch_wide(const GemmArgs &a, int split, bool sw, hipStream_t
   float *partials =
       split > 1 ? (float *)(ws + kTicketBytes + ((pq_operand_bytes(a.M, a.K) + 255) & ~(size_t)255)) : nullptr;
   dim3 grid((unsigned)(n_tiles * m_tiles * split));
-  gemm_wide_kernel<MW, NW, W, D><<<grid, 64 * W, 0, stream>>>(aop, (const uint8_t *)a.Bw, (const uint8_t *)a.Bs,
+  gemm_wide_kernel<MW, NW, W, D, BL><<<grid, 64 * W, 0, stream>>>(aop, (const uint8_t *)a.Bw, (const uint8_t *)a.Bs,
                                                                (uint16_t *)a.C, partials, tickets, a.M, a.N, a.K,
                                                                split, n_tiles, m_tiles);
   return hipGetLastError();
@@ -417,9 +507,15 @@ static hipError_t launch_wide(const GemmArgs &a, int split, bool sw, hipStream_t
 
 #define MXFP4_DEFINE_WIDE(MW, NW, W, D)                                                                          \
   hipError_t launch_wide_##MW##_##NW##_##W##_##D(const GemmArgs &a, int split, bool sw, hipStream_t stream) { \
-    return launch_wide<MW, NW, W, D>(a, split, sw, stream);                                                     \
+    return launch_wide<MW, NW, W, D, false>(a, split, sw, stream);                                              \
   }
 MXFP4_WIDE_VARIANTS(MXFP4_DEFINE_WIDE)
 #undef MXFP4_DEFINE_WIDE
+#define MXFP4_DEFINE_WIDEL(MW, NW, W, D)                                                                          \
+  hipError_t launch_widel_##MW##_##NW##_##W##_##D(const GemmArgs &a, int split, bool sw, hipStream_t stream) { \
+    return launch_wide<MW, NW, W, D, true>(a, split, sw, stream);                                                \
+  }
+MXFP4_WIDEL_VARIANTS(MXFP4_DEFINE_WIDEL)
+#undef MXFP4_DEFINE_WIDEL
 
 }  // namespace mxfp4

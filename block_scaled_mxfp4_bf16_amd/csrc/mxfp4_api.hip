@@ -99,7 +99,7 @@ bool pick_schedule(int M, int N, int K, Schedule *out, bool need_pq = false) {
     for (int v = 0; v < num_gemm_variants(); ++v) {
       Schedule s;
       gemm_variant_shape(v, &s);
-      if (!s.wide) continue;
+      if (s.wide != 1) continue;  // the LDS-staged variants run only when named
       for (s.split = 1; s.split <= 8; ++s.split) {
         if (!covers(s, M, N, K)) continue;
         const int wgs = tiles_of(s, M, N) * s.split;
@@ -160,11 +160,14 @@ bool pick_schedule(int M, int N, int K, Schedule *out, bool need_pq = false) {
 bool parse_name(const char *name, Schedule *out) {
   int mt, nt, wn, wk, kpw, split, used = 0;
   int v;
-  if (strncmp(name, "wide_", 5) == 0) {
+  if (strncmp(name, "wide_", 5) == 0 || strncmp(name, "widel_", 6) == 0) {
+    // wide_: B in registers; widel_: B staged through LDS
+    const int lds = name[4] == 'l';
     int w, d;
-    if (sscanf(name, "wide_mt%d_nt%d_w%d_d%d_split%d%n", &mt, &nt, &w, &d, &split, &used) != 5 || name[used] != 0)
+    if (sscanf(name + (lds ? 6 : 5), "mt%d_nt%d_w%d_d%d_split%d%n", &mt, &nt, &w, &d, &split, &used) != 5 ||
+        name[(lds ? 6 : 5) + used] != 0)
       return false;
-    v = find_gemm_variant(mt, nt, 1, w, d, 1, 16, 1);
+    v = find_gemm_variant(mt, nt, 1, w, d, 1, 16, lds ? 3 : 1);
   } else {
     if (sscanf(name, "mt%d_nt%d_wn%d_wk%d_kpw%d_split%d%n", &mt, &nt, &wn, &wk, &kpw, &split, &used) != 6)
       return false;
@@ -195,7 +198,7 @@ bool parse_schedule(const std::string &name, int M, int N, int K, Schedule *out)
 // The name mxfp4_set_schedule_override accepts for a schedule.
 void schedule_to_name(const Schedule &s, char *buf, size_t n) {
   if (s.wide)
-    snprintf(buf, n, "wide_mt%d_nt%d_w%d_d%d_split%d", s.mt, s.nt, s.wk, s.kpw, s.split);
+    snprintf(buf, n, "%s_mt%d_nt%d_w%d_d%d_split%d", s.wide == 3 ? "widel" : "wide", s.mt, s.nt, s.wk, s.kpw, s.split);
   else
     snprintf(buf, n, "mt%d_nt%d_wn%d_wk%d_kpw%d_split%d%s", s.mt, s.nt, s.wn, s.wk, s.kpw, s.split,
              s.pq ? "_pq" : (s.rb == 8 ? "_r8" : ""));

@@ -21,7 +21,8 @@ namespace mxfp4 {
 //         converts are spent on rows that do not exist)
 //   wide  1: the large-M kernel -- A quantized once, wk waves per
 //         workgroup that split K, each holding the whole 16*mt x 16*nt
-//         tile; kpw is then the number of K steps loaded ahead
+//         tile; kpw is then the number of K steps loaded ahead; 3: the
+//         same kernel with B staged through LDS
 struct Schedule {
   int mt, nt, wn, wk, kpw, split, pq, rb, wide;
   int variant;  // index into the kernel table
@@ -71,6 +72,12 @@ inline size_t pq_operand_bytes(int M, int K) {
   hipError_t launch_wide_##MW##_##NW##_##W##_##D(const GemmArgs &a, int split, bool sw, hipStream_t stream);
 MXFP4_WIDE_VARIANTS(MXFP4_DECLARE_WIDE)
 #undef MXFP4_DECLARE_WIDE
+// ... with B's codes staged through a per-wave LDS ring of D steps.
+#define MXFP4_WIDEL_VARIANTS(X) X(4, 7, 4, 4) X(4, 7, 4, 3) X(4, 4, 8, 2) X(4, 2, 8, 4) X(4, 8, 4, 3)
+#define MXFP4_DECLARE_WIDEL(MW, NW, W, D) \
+  hipError_t launch_widel_##MW##_##NW##_##W##_##D(const GemmArgs &a, int split, bool sw, hipStream_t stream);
+MXFP4_WIDEL_VARIANTS(MXFP4_DECLARE_WIDEL)
+#undef MXFP4_DECLARE_WIDEL
 
 size_t gemm_workspace_bytes(const Schedule &s, int M, int N, int K);
 hipError_t launch_gemm(const Schedule &s, const GemmArgs &a, bool sw_quant, hipStream_t stream);

@@ -169,7 +169,16 @@ def test_wide_schedule_names():
         assert mx.mxfp4_gemm_schedule_name(256, 7168 - 32, 7168) is None  # N not a multiple of 112
     finally:
         mx.mxfp4_set_schedule_override(None)
-    for bad in ("wide_mt4_nt7_w8_d9_split1", "wide_mt3_nt7_w8_d2_split1", "wide_mt4_nt7_w8_d2_split1_pq", "wide_mt4_nt7_d2_split1"):
+    # B staged through LDS: named only, never the default
+    mx.mxfp4_set_schedule_override("widel_mt4_nt7_w4_d4_split1")
+    try:
+        assert mx.mxfp4_gemm_schedule_name(256, 7168, 7168) == "widel_mt4_nt7_w4_d4_split1"
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+    for M, N, K in ((256, 7168, 7168), (128, 2048, 4096), (1024, 7168, 2048)):
+        assert not mx.mxfp4_gemm_schedule_name(M, N, K).startswith("widel_")
+    for bad in ("wide_mt4_nt7_w8_d9_split1", "wide_mt3_nt7_w8_d2_split1", "wide_mt4_nt7_w8_d2_split1_pq", "wide_mt4_nt7_d2_split1",
+                "widel_mt4_nt7_w8_d2_split1", "widel_mt4_nt7_w4_d4_split1_r8", "widl_mt4_nt7_w4_d4_split1"):
         with pytest.raises(RuntimeError):
             mx.mxfp4_set_schedule_override(bad)
 
@@ -187,7 +196,7 @@ def test_every_schedule_the_gpu_tests_name_covers_its_shape():
     from tests import test_gpu_gemm as g
     cases = [(s, M, N, K) for s, M, N, K in g.WIDE_CASES]
     cases += [(s, M, 256, 2048 + 64) for s in g.R8_SCHEDULES for M in (1, 5, 8)]
-    cases += [(s, 70, 224, 1088) for s in ("wide_mt4_nt7_w4_d2_split1", "wide_mt8_nt2_w8_d2_split2")]
+    cases += [(s, 70, 224, 1088) for s in g.RAGGED_SCHEDULES]
     cases += [(s, M, N, K) for s, M, N, K in g.GEMM_Q_CASES]
     try:
         for s in g.SCHEDULES:  # compiled (the test skips those that cannot cover its K)

@@ -193,7 +193,10 @@ def test_workspace_reused_across_shapes_with_more_tiles():
     assert_close(first.run(), first.ref(), "first shape again")
 
 
-@pytest.mark.parametrize("sched", ["wide_mt4_nt7_w4_d2_split1", "wide_mt8_nt2_w8_d2_split2"])
+RAGGED_SCHEDULES = ["wide_mt4_nt7_w4_d2_split1", "wide_mt8_nt2_w8_d2_split2", "widel_mt4_nt7_w4_d3_split1"]
+
+
+@pytest.mark.parametrize("sched", RAGGED_SCHEDULES)
 def test_k_loop_kernels_ragged(sched):
     """K loop with a step count that is not a multiple of the prefetch depth
     or of the waves, a half step (K % 128 == 64), and rows past the last
@@ -240,7 +243,12 @@ WIDE_CASES = [("wide_mt4_nt7_w8_d2_split1", 130, 224, 1088), ("wide_mt4_nt7_w4_d
               ("wide_mt4_nt3_w8_d3_split1", 256, 192, 512), ("wide_mt4_nt6_w8_d2_split4", 96, 192, 4096),
               ("wide_mt4_nt2_w8_d4_split1", 17, 64, 256), ("wide_mt4_nt4_w8_d3_split1", 256, 512, 1024),
               ("wide_mt4_nt8_w8_d2_split5", 80, 256, 2112), ("wide_mt4_nt1_w8_d4_split3", 64, 96, 448),
-              ("wide_mt8_nt3_w8_d2_split1", 140, 96, 8192), ("wide_mt4_nt4_w8_d2_split2", 66, 64, 64)]
+              ("wide_mt8_nt3_w8_d2_split1", 140, 96, 8192), ("wide_mt4_nt4_w8_d2_split2", 66, 64, 64),
+              # B staged through a per-wave LDS ring: a partial first round, several
+              # full rounds, uneven splits
+              ("widel_mt4_nt7_w4_d4_split1", 130, 224, 1088), ("widel_mt4_nt7_w4_d3_split3", 70, 448, 2112),
+              ("widel_mt4_nt4_w8_d2_split1", 256, 512, 1024), ("widel_mt4_nt2_w8_d4_split2", 96, 192, 4096),
+              ("widel_mt4_nt8_w4_d3_split1", 80, 256, 8192), ("widel_mt4_nt7_w4_d4_split1", 200, 448, 7168)]
 
 
 @pytest.mark.parametrize("sched,M,N,K", WIDE_CASES)
@@ -262,7 +270,7 @@ def test_wide_kernel_matches_oracle(sched, M, N, K):
 GEMM_Q_CASES = [("mt4_nt1_wn2_wk4_kpw4_split1_pq", 64, 7168, 2048), ("mt1_nt1_wn1_wk8_kpw4_split2_pq", 8, 2112, 7168),
                 ("mt2_nt1_wn1_wk1_kpw4_split1_pq", 32, 4096, 512), ("mt4_nt2_wn2_wk2_kpw4_split3_pq", 40, 256, 2112),
                 ("wide_mt4_nt7_w4_d2_split1", 130, 224, 1088), ("wide_mt8_nt2_w8_d2_split2", 200, 128, 1600),
-                ("wide_mt4_nt1_w8_d4_split3", 65, 96, 448)]
+                ("wide_mt4_nt1_w8_d4_split3", 65, 96, 448), ("widel_mt4_nt7_w4_d4_split1", 130, 224, 1088)]
 
 
 @pytest.mark.parametrize("sched,M,N,K", GEMM_Q_CASES)
