@@ -31,12 +31,26 @@
 // columns and a run of K steps.  Its waves form a WN x WK grid: WN waves
 // share the staged A and take NT subtiles each; WK waves split the run
 // (KPW steps each) and add their accumulators through LDS in wave order.
-// When one tile's K range is split over `split` workgroups (submission
-// 610679, split-K kernel), each writes its f32 partial tile to the workspace
-// and takes a ticket; the workgroup that draws the last ticket adds the
-// partials in split order, stores bf16 C and resets the ticket.  The sum
-// order is fixed, so results are deterministic, and there is no second
-// launch (the pages reduce split-K partials with a second kernel).
+// When one tile's K range is split over several workgroups (submission
+// 610679, split-K kernel), the partial tiles meet in the workspace; how is
+// the epilogue mode EPI:
+//   0  each workgroup writes its f32 partial tile to a slot of its own and
+//      takes a ticket; the one that draws the last ticket adds the slots in
+//      split order, stores bf16 C and resets the ticket.  The sum order is
+//      fixed, so results are deterministic, and there is no second launch
+//      (the pages reduce split-K partials with a second kernel).
+//   1  each workgroup adds its partial tile into one f32 tile with float
+//      atomics (submission 711914, the fused large-K kernel, adds into a
+//      zeroed f32 C and casts it afterwards); the last ticket casts the sum
+//      to bf16 and stores C.  The order of the additions, and so the
+//      rounding, varies from run to run.  The f32 tiles are zero-filled by
+//      a small launch before the GEMM.
+//   2  stream-K: a grid of G workgroups splits the tiles x K steps
+//      iteration space into G equal contiguous runs, so every workgroup has
+//      the same work whatever the tile count.  A run may cross tile
+//      boundaries; a tile that one run covers whole is stored directly, the
+//      others go through ticketed slots as in mode 0, added in workgroup
+//      order, so results are deterministic.
 #include <type_traits>
 
 #include "mxfp4_device.hpp"
@@ -44,7 +58,8 @@
 
 namespace mxfp4 {
 
-template <int MT, int NT, int WN, int WK, int KPW, bool PREQ, int RB>
+// `split`: workgroups per tile (EPI 0, 1) or of the whole grid (EPI 2).
+template <int MT, int NT, int WN, int WK, int KPW, bool PREQ, int RB, int EPI>
 __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__restrict__ A,
                                                            const uint8_t *__restrict__ Aop,
                                                            const uint8_t *__restrict__ Bw,
@@ -74,21 +89,12 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
   uint8_t *s_lds = lds + A_BYTES;
   float *red = (float *)lds;
 
+  constexpr int EPT = (E + NTH - 1) / NTH;         // tile elements per thread in the split epilogue
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave % WN;
   const int wk = wave / WN;
-  const int bid = blockIdx.x;
-  const int n_tile = bid % n_tiles;
-  const int rest = bid / n_tiles;
-  const int sk = rest % split;
-  const int m_tile = rest / split;
-  const int m0 = m_tile * 16 * MT;
-  const int gw = n_tile * TN + wn * NT;  // this wave's first 16-row group of B
-
   const int KS = (K + 127) >> 7;
-  const int S0 = (int)((uint32_t)(sk * KS) / (uint32_t)split);
-  const int S1 = (int)((uint32_t)((sk + 1) * KS) / (uint32_t)split);
   const int gp = ((K >> 5) + 7) & ~7;
 
   // Buffer descriptors carry the operands' byte sizes: a load whose offset
@@ -101,6 +107,14 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, a_bytes, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Bw, 0, b_bytes, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Bs, 0, s_bytes, kRsrcWord3);
+
+  // One segment: steps [S0, S1) of tile (m_tile, n_tile), whose K range is
+  // shared by `nparts` workgroups; slot(j) is the partial tile of the j-th
+  // of them and this workgroup is number `mine_j`.
+  auto segment = [&](const int m_tile, const int n_tile, const int S0, const int S1, const int nparts,
+                     const int mine_j, auto slot) {
+  const int m0 = m_tile * 16 * MT;
+  const int gw = n_tile * TN + wn * NT;  // this wave's first 16-row group of B
 
   // Phase 1: issue the loads.  A first: it is small and mostly L2-resident,
   // and since the load counter retires in issue order, quantizing it can
@@ -122,7 +136,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
       const int row = m0 + 16 * mt + (RB == 8 ? (lane >> 3) : (lane >> 2));
       const int kel = ks * 128 + ch * 32 + (lane & 3) * 8;
       const bool ok = (unit < UNITS) && (ks < S1) && (row < M) && (ks * 128 + ch * 32 < K);
-      aw[u] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ok ? (row * K + kel) * 2 : a_bytes, 0, 0);
+      aw[u] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off_or_oob(ok, (row * K + kel) * 2), 0, 0);
     }
   } else {
     // pre-quantized A in operand blocks: per (m tile, step) 1 KiB of codes,
@@ -137,8 +151,8 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
         const int mtile = m_tile * MT + mt;
         const bool ok = (ks < S1) && (mtile * 16 < M);
         const int blk = (mtile * KS + ks) * 1088;
-        ap[i][mt] = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, ok ? blk + lane * 16 : op_bytes, 0, 0);
-        asb[i][mt] = __builtin_amdgcn_raw_buffer_load_b8(q_rsrc, ok ? blk + 1024 + lane : op_bytes, 0, 0);
+        ap[i][mt] = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, off_or_oob(ok, blk + lane * 16), 0, 0);
+        asb[i][mt] = __builtin_amdgcn_raw_buffer_load_b8(q_rsrc, off_or_oob(ok, blk + 1024 + lane), 0, 0);
       }
     }
   }
@@ -151,13 +165,13 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
     const bool ok = step_ok && (ks * 128 + kc * 32 < K);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int off = ok ? (gw + nt) * K * 8 + ks * 1024 + lane * 16 : b_bytes;
+      const int off = off_or_oob(ok, (gw + nt) * K * 8 + ks * 1024 + lane * 16);
       bv[i][nt] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, off, 0, 0);
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int g = gw + 2 * p;
-      const int off = step_ok ? (g >> 1) * gp * 32 + (ks >> 1) * 256 + lane * 4 : s_bytes;
+      const int off = off_or_oob(step_ok, (g >> 1) * gp * 32 + (ks >> 1) * 256 + lane * 4);
       sword[i][p] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, off, 0, 0);
     }
   }
@@ -264,7 +278,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
   auto elem = [&](int mt, int nt, int r) { return (((mt * WN + wn) * NT + nt) * 4 + r) * 64 + lane; };
 
   if constexpr (WK == 1) {
-    if (split == 1) {
+    if (nparts == 1) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -283,7 +297,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
 #pragma unroll
         for (int r = 0; r < 4; ++r) red[wk * E + elem(mt, nt, r)] = acc[mt][nt][r];
     __syncthreads();
-    if (split == 1) {
+    if (nparts == 1) {
       // eight consecutive elements are eight consecutive columns of one row:
       // add them over the WK waves and store them as one 16-byte write
       for (int j = threadIdx.x; j < E / 8; j += NTH) {
@@ -316,45 +330,112 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
     }
   }
 
-  // Split K across workgroups.  Each writes its partial tile to its own slot
-  // with device-coherent stores, waits until they have completed, and takes
-  // a ticket; the workgroup that draws the last ticket reads every slot with
-  // device-coherent loads, adds them in slot order and stores C.  Only these
-  // accesses touch the workspace, so no cache-wide write-back is needed.
-  float *mine = partials + ((size_t)tile * split + sk) * E;
+  // Split K across workgroups.  Each writes its partial tile with
+  // device-coherent stores (EPI 1: float atomics), waits until they have
+  // completed, and takes a ticket; the workgroup that draws the last ticket
+  // reads the partials with device-coherent loads, adds them in slot order
+  // and stores C.  Only these accesses touch the workspace, so no
+  // cache-wide write-back is needed.
+  float *const mine = EPI == 1 ? partials + (size_t)tile * E : slot(mine_j);
+  auto put = [&](int e, float v) {
+    if constexpr (EPI == 1)
+      __hip_atomic_fetch_add(mine + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      __hip_atomic_store(mine + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   if constexpr (WK == 1) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          __hip_atomic_store(mine + elem(mt, nt, r), acc[mt][nt][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int r = 0; r < 4; ++r) put(elem(mt, nt, r), acc[mt][nt][r]);
   } else {
     for (int e = threadIdx.x; e < E; e += NTH) {
-      float s = 0.f;
+      float v = 0.f;
 #pragma unroll
-      for (int w = 0; w < WK; ++w) s += red[w * E + e];
-      __hip_atomic_store(mine + e, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int w = 0; w < WK; ++w) v += red[w * E + e];
+      put(e, v);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's slot stores have completed
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's workspace writes have completed
   __syncthreads();
   if (threadIdx.x == 0)
     s_last = __hip_atomic_fetch_add(&tickets[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                     (uint32_t)(split - 1)
+                     (uint32_t)(nparts - 1)
                  ? 1u
                  : 0u;
   __syncthreads();
   if (!s_last) return;
-  const float *all = partials + (size_t)tile * split * E;
-  for (int e = threadIdx.x; e < E; e += NTH) {
-    float s = 0.f;
-    for (int j = 0; j < split; ++j)
-      s += __hip_atomic_load(all + (size_t)j * E + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    store_c(e, s);
+  float sum[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) sum[i] = 0.f;
+  for (int j = 0; j < (EPI == 1 ? 1 : nparts); ++j) {
+    const float *part = EPI == 1 ? mine : slot(j);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = threadIdx.x + i * NTH;
+      if (EPT * NTH == E || e < E) sum[i] += __hip_atomic_load(part + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = threadIdx.x + i * NTH;
+    if (EPT * NTH == E || e < E) store_c(e, sum[i]);
   }
   if (threadIdx.x == 0) __hip_atomic_store(&tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };  // segment
+
+  if constexpr (EPI == 2) {
+    // Workgroup g owns iterations [start(g), start(g+1)) of the tiles x K
+    // steps space, tile-major; each run is at most one workgroup's K
+    // capacity long (the host checks), so a tile it covers in part is its
+    // first or its last, and it keeps those partials in its slots 2g and
+    // 2g + 1.
+    const int m_tiles = (M + 16 * MT - 1) / (16 * MT);
+    const long long T = (long long)n_tiles * m_tiles * KS;
+    const int G = split;
+    auto start = [&](int g) { return (long long)g * T / G; };
+    // the workgroup whose run holds iteration x: the largest g with
+    // start(g) <= x; x*G/T is at most one below it
+    auto owner = [&](long long x) {
+      int g = (int)(x * G / T);
+      if (g + 1 < G && start(g + 1) <= x) ++g;
+      return g;
+    };
+    const int g = blockIdx.x;
+    const long long end = start(g + 1);
+    for (long long it = start(g); it < end;) {
+      const int t = (int)(it / KS);
+      const int s0 = (int)(it - (long long)t * KS);
+      const int s1 = (int)((long long)KS < s0 + (end - it) ? (long long)KS : s0 + (end - it));
+      const int glo = owner((long long)t * KS), ghi = owner((long long)t * KS + KS - 1);
+      auto slot = [&](int j) {
+        const int gg = glo + j;
+        const int which = (int)(start(gg) / KS) == t ? 0 : 1;
+        return partials + ((size_t)gg * 2 + which) * E;
+      };
+      segment(t / n_tiles, t - (t / n_tiles) * n_tiles, s0, s1, ghi - glo + 1, g - glo, slot);
+      it += s1 - s0;
+      __syncthreads();  // LDS and s_last are reused by the next segment
+    }
+  } else {
+    const int bid = blockIdx.x;
+    const int n_tile = bid % n_tiles;
+    const int rest = bid / n_tiles;
+    const int sk = rest % split;
+    const int m_tile = rest / split;
+    const int tile = m_tile * n_tiles + n_tile;
+    auto slot = [&](int j) { return partials + ((size_t)tile * split + j) * E; };
+    segment(m_tile, n_tile, (int)((uint32_t)(sk * KS) / (uint32_t)split),
+            (int)((uint32_t)((sk + 1) * KS) / (uint32_t)split), split, sk, slot);
+  }
+}
+
+// Zero-fills the f32 tiles the atomic split-K epilogue adds into.
+__global__ __launch_bounds__(256) void zero_f32_kernel(float *__restrict__ p, int n4) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n4) ((v4f *)p)[i] = v4f{0.f, 0.f, 0.f, 0.f};
 }
 
 // A quantized once into operand blocks for the pre-quantized mode: block
@@ -415,7 +496,7 @@ size_t operand_a_bytes(int M, int K) { return (size_t)((M + 15) / 16) * (size_t)
 
 typedef hipError_t (*launch_fn)(const GemmArgs &, int split, bool sw, hipStream_t);
 
-template <int MT, int NT, int WN, int WK, int KPW, bool PREQ, int RB>
+template <int MT, int NT, int WN, int WK, int KPW, bool PREQ, int RB, int EPI = 0>
 static hipError_t launch_variant(const GemmArgs &a, int split, bool sw, hipStream_t stream) {
   const int n_tiles = a.N / (16 * NT * WN);
   const int m_tiles = (a.M + 16 * MT - 1) / (16 * MT);
@@ -436,10 +517,16 @@ static hipError_t launch_variant(const GemmArgs &a, int split, bool sw, hipStrea
   }
   uint32_t *tickets = (uint32_t *)ws;
   float *partials = nullptr;
-  if (split > 1)
+  if (split > 1 || EPI == 2)
     partials = (float *)(ws + kTicketBytes + (PREQ ? ((pq_operand_bytes(a.M, a.K) + 255) & ~(size_t)255) : 0));
-  dim3 grid((unsigned)(n_tiles * m_tiles * split));
-  gemm_kernel<MT, NT, WN, WK, KPW, PREQ, RB><<<grid, 64 * WN * WK, 0, stream>>>(
+  if (EPI == 1 && split > 1) {
+    const int n4 = n_tiles * m_tiles * MT * NT * WN * 64;  // tiles x elements / 4
+    zero_f32_kernel<<<(n4 + 255) / 256, 256, 0, stream>>>(partials, n4);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid((unsigned)(EPI == 2 ? split : n_tiles * m_tiles * split));
+  gemm_kernel<MT, NT, WN, WK, KPW, PREQ, RB, EPI><<<grid, 64 * WN * WK, 0, stream>>>(
       (const uint16_t *)a.A, aop, (const uint8_t *)a.Bw, (const uint8_t *)a.Bs, (uint16_t *)a.C, partials, tickets, a.M,
       a.N, a.K, split, n_tiles, sw ? 1 : 0);
   return hipGetLastError();
@@ -450,19 +537,27 @@ struct Variant {
   launch_fn fn;
   int rb;    // rows per staged A block (8: only for M <= 8)
   int wide;  // the large-M kernel of gemm_wide.hip
+  int epi;   // split epilogue: 0 ticketed slots, 1 float atomics, 2 stream-K
 };
 
-#define V(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 0, launch_variant<MT, NT, WN, WK, KPW, false, 16>, 16, 0}
-#define V8(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 0, launch_variant<MT, NT, WN, WK, KPW, false, 8>, 8, 0}
-#define VQ(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 1, launch_variant<MT, NT, WN, WK, KPW, true, 16>, 16, 0}
+#define V(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 0, launch_variant<MT, NT, WN, WK, KPW, false, 16>, 16, 0, 0}
+#define V8(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 0, launch_variant<MT, NT, WN, WK, KPW, false, 8>, 8, 0, 0}
+#define VQ(MT, NT, WN, WK, KPW) {MT, NT, WN, WK, KPW, 1, launch_variant<MT, NT, WN, WK, KPW, true, 16>, 16, 0, 0}
+// the same kernels with the float-atomic (EPI 1) and stream-K (EPI 2)
+// epilogues, for the long-K small-M shapes that split K
+#define VE(MT, NT, WN, WK, KPW, RB)                                                              \
+  {MT, NT, WN, WK, KPW, 0, launch_variant<MT, NT, WN, WK, KPW, false, RB, 1>, RB, 0, 1},        \
+      {MT, NT, WN, WK, KPW, 0, launch_variant<MT, NT, WN, WK, KPW, false, RB, 2>, RB, 0, 2},
 // large-M kernels: W waves split K; listed with wn = 1, wk = W, kpw = the
 // number of steps loaded ahead
-#define VW(MW, NW, W, D) {MW, NW, 1, W, D, 1, launch_wide_##MW##_##NW##_##W##_##D, 16, 1},
-#define VWL(MW, NW, W, D) {MW, NW, 1, W, D, 1, launch_widel_##MW##_##NW##_##W##_##D, 16, 3},
+#define VW(MW, NW, W, D) {MW, NW, 1, W, D, 1, launch_wide_##MW##_##NW##_##W##_##D, 16, 1, 0},
+#define VWL(MW, NW, W, D) {MW, NW, 1, W, D, 1, launch_widel_##MW##_##NW##_##W##_##D, 16, 3, 0},
 
 static const Variant kVariants[] = {
     MXFP4_WIDE_VARIANTS(VW)
     MXFP4_WIDEL_VARIANTS(VWL)
+    VE(1, 2, 1, 8, 4, 16) VE(1, 1, 4, 4, 4, 16) VE(1, 2, 1, 8, 2, 16) VE(1, 1, 1, 8, 4, 16) VE(1, 2, 1, 4, 4, 16)
+    VE(1, 1, 2, 4, 4, 16) VE(1, 2, 4, 4, 4, 16) VE(1, 2, 1, 8, 4, 8) VE(1, 1, 1, 8, 4, 8) VE(1, 1, 4, 4, 4, 8)
     V8(1, 1, 1, 16, 4), V8(1, 1, 1, 14, 4), V8(1, 1, 1, 8, 4), V8(1, 1, 1, 16, 2), V8(1, 1, 2, 8, 4), V8(1, 1, 2, 8, 2),
     V8(1, 2, 1, 16, 4), V8(1, 2, 1, 8, 4), V8(1, 1, 1, 4, 4), V8(1, 1, 1, 4, 2), V8(1, 1, 1, 8, 2), V8(1, 1, 1, 4, 1),
     V8(1, 1, 2, 4, 2), V8(1, 1, 4, 4, 4), V8(1, 1, 1, 2, 2), V8(1, 1, 1, 1, 4), V8(1, 1, 1, 2, 4),
@@ -521,6 +616,7 @@ static const Variant kVariants[] = {
 #undef V
 #undef VW
 #undef VWL
+#undef VE
 #undef V8
 #undef VQ
 
@@ -535,26 +631,31 @@ void gemm_variant_shape(int v, Schedule *s) {
   s->pq = kVariants[v].pq;
   s->rb = kVariants[v].rb;
   s->wide = kVariants[v].wide;
+  s->epi = kVariants[v].epi;
   s->variant = v;
 }
 
-int find_gemm_variant(int mt, int nt, int wn, int wk, int kpw, int pq, int rb, int wide) {
+int find_gemm_variant(int mt, int nt, int wn, int wk, int kpw, int pq, int rb, int wide, int epi) {
   for (int v = 0; v < num_gemm_variants(); ++v)
     if (kVariants[v].mt == mt && kVariants[v].nt == nt && kVariants[v].wn == wn && kVariants[v].wk == wk &&
-        kVariants[v].kpw == kpw && kVariants[v].pq == pq && kVariants[v].rb == rb && kVariants[v].wide == wide)
+        kVariants[v].kpw == kpw && kVariants[v].pq == pq && kVariants[v].rb == rb && kVariants[v].wide == wide &&
+        kVariants[v].epi == epi)
       return v;
   return -1;
 }
 
 size_t gemm_workspace_bytes(const Schedule &s, int M, int N, int K) {
-  if (s.split <= 1 && !s.pq) return 0;
+  if (s.split <= 1 && !s.pq && s.epi != 2) return 0;
   size_t bytes = kTicketBytes;
   if (s.pq) bytes += (pq_operand_bytes(M, K) + 255) & ~(size_t)255;
-  if (s.split > 1) {
-    const size_t tiles = (size_t)(N / (16 * s.nt * s.wn)) * (size_t)((M + 16 * s.mt - 1) / (16 * s.mt));
-    const size_t e = (size_t)s.mt * s.nt * s.wn * 256;
+  const size_t tiles = (size_t)(N / (16 * s.nt * s.wn)) * (size_t)((M + 16 * s.mt - 1) / (16 * s.mt));
+  const size_t e = (size_t)s.mt * s.nt * s.wn * 256;
+  if (s.epi == 2)
+    bytes += (size_t)s.split * 2 * e * sizeof(float);  // two slots per workgroup of the grid
+  else if (s.epi == 1 && s.split > 1)
+    bytes += tiles * e * sizeof(float);  // one f32 tile per output tile
+  else if (s.split > 1)
     bytes += tiles * (size_t)s.split * e * sizeof(float);
-  }
   return bytes;
 }
 

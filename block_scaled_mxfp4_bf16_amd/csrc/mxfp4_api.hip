@@ -49,6 +49,13 @@ bool covers(const Schedule &s, int M, int N, int K) {
   if (s.split < 1 || N % (16 * s.nt * s.wn) != 0) return false;
   if (s.rb == 8 && (M > 8 || s.mt != 1)) return false;
   const int ks = (K + 127) / 128;
+  if (s.epi == 2) {
+    // stream-K: every workgroup has at least one iteration and at most the
+    // K steps one workgroup covers; tickets for every tile
+    const int64_t T = (int64_t)tiles_of(s, M, N) * ks;
+    return s.split <= kMaxStreamKGroups && s.split <= T && (T + s.split - 1) / s.split <= s.wk * s.kpw &&
+           tiles_of(s, M, N) <= kMaxSplitTiles;
+  }
   // the wide kernel loops over K; the others cover wk * kpw steps per split
   if (!s.wide && (ks + s.split - 1) / s.split > s.wk * s.kpw) return false;
   if (s.split > 1 && tiles_of(s, M, N) > kMaxSplitTiles) return false;
@@ -131,7 +138,7 @@ bool pick_schedule(int M, int N, int K, Schedule *out, bool need_pq = false) {
   for (int v = 0; v < num_gemm_variants(); ++v) {
     Schedule s;
     gemm_variant_shape(v, &s);
-    if (s.mt != mt || s.pq != (need_pq ? 1 : 0) || s.wide) continue;
+    if (s.mt != mt || s.pq != (need_pq ? 1 : 0) || s.wide || s.epi) continue;  // atomic and stream-K: named only
     if (!need_pq && (s.rb == 8) != (M <= 8)) continue;
     for (s.split = 1; s.split <= 16; ++s.split) {
       if (!covers(s, M, N, K)) continue;
@@ -169,18 +176,29 @@ bool parse_name(const char *name, Schedule *out) {
       return false;
     v = find_gemm_variant(mt, nt, 1, w, d, 1, 16, lds ? 3 : 1);
   } else {
-    if (sscanf(name, "mt%d_nt%d_wn%d_wk%d_kpw%d_split%d%n", &mt, &nt, &wn, &wk, &kpw, &split, &used) != 6)
-      return false;
+    // "..._split<n>" with "_pq", "_r8", "_at" or "_r8_at" appended, or
+    // "..._streamk<G>" with "_r8" appended
+    int epi = 0;
+    if (sscanf(name, "mt%d_nt%d_wn%d_wk%d_kpw%d_split%d%n", &mt, &nt, &wn, &wk, &kpw, &split, &used) != 6) {
+      used = 0;
+      if (sscanf(name, "mt%d_nt%d_wn%d_wk%d_kpw%d_streamk%d%n", &mt, &nt, &wn, &wk, &kpw, &split, &used) != 6)
+        return false;
+      epi = 2;
+    }
     int pq = 0, rb = 16;
     const char *rest = name + used;
-    if (strcmp(rest, "_pq") == 0) {
-      pq = 1;
-    } else if (strcmp(rest, "_r8") == 0) {
+    if (strncmp(rest, "_r8", 3) == 0) {
       rb = 8;
+      rest += 3;
+    }
+    if (strcmp(rest, "_pq") == 0 && rb == 16 && epi == 0) {
+      pq = 1;
+    } else if (strcmp(rest, "_at") == 0 && epi == 0) {
+      epi = 1;
     } else if (*rest != 0) {
       return false;
     }
-    v = find_gemm_variant(mt, nt, wn, wk, kpw, pq, rb, 0);
+    v = find_gemm_variant(mt, nt, wn, wk, kpw, pq, rb, 0, epi);
   }
   if (v < 0 || split < 1) return false;
   gemm_variant_shape(v, out);
@@ -200,8 +218,9 @@ void schedule_to_name(const Schedule &s, char *buf, size_t n) {
   if (s.wide)
     snprintf(buf, n, "%s_mt%d_nt%d_w%d_d%d_split%d", s.wide == 3 ? "widel" : "wide", s.mt, s.nt, s.wk, s.kpw, s.split);
   else
-    snprintf(buf, n, "mt%d_nt%d_wn%d_wk%d_kpw%d_split%d%s", s.mt, s.nt, s.wn, s.wk, s.kpw, s.split,
-             s.pq ? "_pq" : (s.rb == 8 ? "_r8" : ""));
+    snprintf(buf, n, "mt%d_nt%d_wn%d_wk%d_kpw%d_%s%d%s%s", s.mt, s.nt, s.wn, s.wk, s.kpw,
+             s.epi == 2 ? "streamk" : "split", s.split, s.pq ? "_pq" : (s.rb == 8 ? "_r8" : ""),
+             s.epi == 1 ? "_at" : "");
 }
 
 bool choose(int M, int N, int K, Schedule *s, bool need_pq = false) {

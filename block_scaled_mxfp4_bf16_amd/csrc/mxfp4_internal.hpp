@@ -23,8 +23,14 @@ namespace mxfp4 {
 //         workgroup that split K, each holding the whole 16*mt x 16*nt
 //         tile; kpw is then the number of K steps loaded ahead; 3: the
 //         same kernel with B staged through LDS
+//   epi   how split K partials meet: 0 ticketed slots added in split
+//         order; 1 float atomics into one f32 tile (zero-filled by a launch
+//         of its own); 2 stream-K -- `split` is then the number of
+//         workgroups of the whole grid, each taking an equal run of the
+//         tiles x K steps iterations
 struct Schedule {
   int mt, nt, wn, wk, kpw, split, pq, rb, wide;
+  int epi;
   int variant;  // index into the kernel table
 };
 
@@ -34,6 +40,8 @@ struct Schedule {
 // another without the partials of one landing on the tickets of the next.
 constexpr size_t kTicketBytes = 65536;
 constexpr int kMaxSplitTiles = (int)(kTicketBytes / 4);
+// Largest stream-K grid (its partials take two tiles per workgroup).
+constexpr int kMaxStreamKGroups = 8192;
 
 struct GemmArgs {
   const void *A;
@@ -51,7 +59,7 @@ struct GemmArgs {
 // Kernel table queries (gemm_kernels.hip).
 int num_gemm_variants();
 void gemm_variant_shape(int v, Schedule *s);  // fills everything but split
-int find_gemm_variant(int mt, int nt, int wn, int wk, int kpw, int pq, int rb, int wide);
+int find_gemm_variant(int mt, int nt, int wn, int wk, int kpw, int pq, int rb, int wide, int epi = 0);
 
 // Bytes of pre-quantized A in the workspace: the larger of the two operand
 // layouts (the fused kernels' 1088-byte blocks, the large-M kernel's

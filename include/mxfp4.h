@@ -166,7 +166,8 @@ MXFP4_API const char *mxfp4_gemm_q_schedule_name(int64_t M, int64_t N, int64_t K
 /* mxfp4_gemm uses a library-owned workspace per (device, stream), created   */
 /* on the first call for a shape that needs more (that call allocates;       */
 /* later calls do not).  Results are deterministic: the split-K partial sums */
-/* are added in a fixed order.                                               */
+/* are added in a fixed order (unless an "_at" schedule is forced by         */
+/* mxfp4_set_schedule_override: its float atomics add in arrival order).     */
 /* Errors: INVALID_ARG (null, M/N/K < 1, misaligned);                        */
 /*         UNSUPPORTED (K % 64 != 0 -- the harness's precondition, submission */
 /*         608632 input generator --, N % 32 != 0, sizes beyond 2^31 bytes); */
@@ -214,8 +215,18 @@ MXFP4_API mxfp4_status_t mxfp4_set_quant_mode(int mode);
 
 /* Process-wide schedule override for mxfp4_gemm, by the name format of
  * mxfp4_gemm_schedule_name (for tuning sweeps); NULL or "" restores the
- * built-in choice.  A call whose shape the override cannot serve returns
- * UNSUPPORTED.  Errors: INVALID_ARG for a name no compiled kernel matches. */
+ * built-in choice.  Besides the names the built-in choice gives, it takes
+ * the split-K epilogues the built-in choice never picks:
+ *   "..._split<n>_at" (or "_r8_at"): the partial tiles are added with f32
+ *       atomics into a workspace tile that a separate launch zero-fills
+ *       first (submission 711914, the fused large-K kernel, adds into a
+ *       zeroed f32 C); the last workgroup of a tile casts it to bf16.  Not
+ *       deterministic: the additions happen in arrival order.
+ *   "mt.._kpw<k>_streamk<G>" (or "_r8"): stream-K, G workgroups each taking
+ *       an equal run of the tiles x K steps iterations; deterministic.
+ *   "widel_...": the large-M kernel with B staged through LDS.
+ * A call whose shape the override cannot serve returns UNSUPPORTED.
+ * Errors: INVALID_ARG for a name no compiled kernel matches. */
 MXFP4_API mxfp4_status_t mxfp4_set_schedule_override(const char *name);
 
 #ifdef __cplusplus

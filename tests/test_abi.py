@@ -198,6 +198,7 @@ def test_every_schedule_the_gpu_tests_name_covers_its_shape():
     cases += [(s, M, 256, 2048 + 64) for s in g.R8_SCHEDULES for M in (1, 5, 8)]
     cases += [(s, 70, 224, 1088) for s in g.RAGGED_SCHEDULES]
     cases += [(s, M, N, K) for s, M, N, K in g.GEMM_Q_CASES]
+    cases += [(s, M, N, K) for s, M, N, K in g.STREAMK_CASES + g.ATOMIC_CASES]
     try:
         for s in g.SCHEDULES:  # compiled (the test skips those that cannot cover its K)
             mx.mxfp4_set_schedule_override(s)
@@ -206,3 +207,42 @@ def test_every_schedule_the_gpu_tests_name_covers_its_shape():
             assert mx.mxfp4_gemm_schedule_name(M, N, K) == s, (s, M, N, K)
     finally:
         mx.mxfp4_set_schedule_override(None)
+
+
+def test_split_epilogue_schedule_names_cover_and_size():
+    """Float-atomic ("_at") and stream-K ("streamk<G>") schedules: accepted
+    only in their own name forms, never picked by default, refused where a
+    workgroup's run would exceed its K capacity or the grid exceeds the
+    iterations, and sized as their layouts say."""
+    # 40x256x2112, 32-column tiles: 24 tiles x 17 steps = 408 iterations;
+    # one workgroup covers wk*kpw = 32 steps; a tile holds 16x32 f32
+    M, N, K = 40, 256, 2112
+    e = 16 * 32 * 4
+    try:
+        mx.mxfp4_set_schedule_override("mt1_nt2_wn1_wk8_kpw4_streamk13")
+        assert mx.mxfp4_gemm_schedule_name(M, N, K) == "mt1_nt2_wn1_wk8_kpw4_streamk13"
+        assert mx.mxfp4_gemm_workspace_bytes(M, N, K) == 65536 + 13 * 2 * e
+        mx.mxfp4_set_schedule_override("mt1_nt2_wn1_wk8_kpw4_streamk12")  # runs of 34 > 32 steps
+        assert mx.mxfp4_gemm_schedule_name(M, N, K) is None
+        mx.mxfp4_set_schedule_override("mt1_nt2_wn1_wk8_kpw4_streamk409")  # more workgroups than iterations
+        assert mx.mxfp4_gemm_schedule_name(M, N, K) is None
+        mx.mxfp4_set_schedule_override("mt1_nt2_wn1_wk8_kpw4_streamk408")
+        assert mx.mxfp4_gemm_schedule_name(M, N, K) == "mt1_nt2_wn1_wk8_kpw4_streamk408"
+        mx.mxfp4_set_schedule_override("mt1_nt2_wn1_wk8_kpw4_split3_at")
+        assert mx.mxfp4_gemm_schedule_name(M, N, K) == "mt1_nt2_wn1_wk8_kpw4_split3_at"
+        assert mx.mxfp4_gemm_workspace_bytes(M, N, K) == 65536 + 24 * e  # one f32 tile per output tile
+        mx.mxfp4_set_schedule_override("mt1_nt2_wn1_wk8_kpw4_split3")
+        assert mx.mxfp4_gemm_workspace_bytes(M, N, K) == 65536 + 24 * 3 * e
+        mx.mxfp4_set_schedule_override("mt1_nt2_wn1_wk8_kpw4_streamk50_r8")
+        assert mx.mxfp4_gemm_schedule_name(5, N, K) == "mt1_nt2_wn1_wk8_kpw4_streamk50_r8"
+        assert mx.mxfp4_gemm_schedule_name(9, N, K) is None  # 8-row staging is for M <= 8
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+    for bad in ("mt1_nt2_wn1_wk8_kpw4_split3_pq_at", "mt1_nt2_wn1_wk8_kpw4_split3_at_r8",
+                "mt1_nt2_wn1_wk8_kpw4_streamk13_at", "mt1_nt2_wn1_wk8_kpw4_streamk13_pq",
+                "mt1_nt2_wn1_wk8_kpw4_streamk0", "mt2_nt2_wn1_wk8_kpw4_streamk13", "mt1_nt2_wn1_wk8_kpw3_split3_at"):
+        with pytest.raises(RuntimeError):
+            mx.mxfp4_set_schedule_override(bad)
+    for shape in ((40, 256, 2112), (8, 2112, 7168), (16, 2112, 7168), (16, 3072, 1536), (64, 7168, 2048)):
+        name = mx.mxfp4_gemm_schedule_name(*shape)
+        assert "streamk" not in name and not name.endswith("_at"), (shape, name)

@@ -193,6 +193,80 @@ def test_workspace_reused_across_shapes_with_more_tiles():
     assert_close(first.run(), first.ref(), "first shape again")
 
 
+# The split-K epilogues the built-in choice never picks.  Stream-K: G
+# workgroups, each an equal run of the tiles x K steps iterations; at
+# 40x256x2112 with 32-column tiles there are 24 tiles x 17 steps = 408
+# iterations, so G = 13 gives runs of 31-32 steps (whole tiles stored
+# directly plus partial ones), 24 one whole tile each, 50 runs of 8-9 steps
+# that cross tile boundaries; with 64-column tiles (12 tiles, 204
+# iterations) G = 204 gives every tile 17 one-step contributors.
+STREAMK_CASES = [("mt1_nt2_wn1_wk8_kpw4_streamk13", 40, 256, 2112), ("mt1_nt2_wn1_wk8_kpw4_streamk24", 40, 256, 2112),
+                 ("mt1_nt2_wn1_wk8_kpw4_streamk50", 40, 256, 2112), ("mt1_nt1_wn4_wk4_kpw4_streamk204", 40, 256, 2112),
+                 ("mt1_nt1_wn4_wk4_kpw4_streamk7_r8", 5, 256, 2112), ("mt1_nt2_wn1_wk8_kpw4_streamk256_r8", 8, 2112, 7168),
+                 ("mt1_nt2_wn1_wk8_kpw2_streamk300", 16, 3072, 1536), ("mt1_nt2_wn4_wk4_kpw4_streamk256", 64, 7168, 2048),
+                 ("mt1_nt1_wn2_wk4_kpw4_streamk97", 17, 128, 4160)]
+# Float-atomic split-K: uneven splits, a half step at the end of K, rows past M.
+ATOMIC_CASES = [("mt1_nt2_wn1_wk8_kpw4_split3_at", 40, 256, 2112), ("mt1_nt1_wn4_wk4_kpw4_split5_at", 33, 128, 4160),
+                ("mt1_nt2_wn1_wk8_kpw4_split2_r8_at", 8, 2112, 7168), ("mt1_nt1_wn4_wk4_kpw4_split4_r8_at", 3, 128, 2112),
+                ("mt1_nt2_wn1_wk4_kpw4_split4_at", 16, 2112, 7168)]
+
+
+def run_forced(c, sched, times):
+    mx.mxfp4_set_schedule_override(sched)
+    try:
+        assert mx.mxfp4_gemm_schedule_name(c.M, c.N, c.K) == sched
+        return [c.run() for _ in range(times)]
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+
+
+@pytest.mark.parametrize("sched,M,N,K", STREAMK_CASES)
+def test_streamk_matches_oracle_and_is_deterministic(sched, M, N, K):
+    torch = torch_cuda()
+    c = make(torch, M, N, K, seed=M + N + K + 5)
+    runs = run_forced(c, sched, 3)
+    assert np.array_equal(runs[0], runs[1]) and np.array_equal(runs[0], runs[2])
+    assert_close(runs[0], c.ref(), "%s %dx%dx%d" % (sched, M, N, K))
+
+
+@pytest.mark.parametrize("sched,M,N,K", ATOMIC_CASES)
+def test_atomic_split_matches_oracle(sched, M, N, K):
+    """Every run within tolerance of the oracle; runs may differ in the
+    last bits, since the atomics add in arrival order.  In between, a
+    ticketed split-K call on another shape leaves its partial sums in the
+    same workspace: the zero-fill launch must clear them."""
+    torch = torch_cuda()
+    c = make(torch, M, N, K, seed=M + N + K + 6)
+    ref = c.ref()
+    for r in run_forced(c, sched, 2):
+        assert_close(r, ref, sched)
+    other = make(torch, 40, 256, 2112, seed=8)
+    for r in run_forced(other, "mt1_nt1_wn1_wk4_kpw1_split17", 1):
+        assert_close(r, other.ref(), "ticketed split between atomic runs")
+    for r in run_forced(c, sched, 1):
+        assert_close(r, ref, sched + " after another shape")
+
+
+@pytest.mark.parametrize("sched,M,N,K", [STREAMK_CASES[2], STREAMK_CASES[5], ATOMIC_CASES[0], ATOMIC_CASES[2]])
+def test_split_epilogues_in_an_exact_caller_workspace(sched, M, N, K):
+    """mxfp4_gemm_ex with a workspace of exactly the size the library asks
+    for, its partial-sum region filled with non-zero bytes."""
+    torch = torch_cuda()
+    c = make(torch, M, N, K, seed=M + N + K + 7)
+    mx.mxfp4_set_schedule_override(sched)
+    try:
+        need = mx.mxfp4_gemm_workspace_bytes(M, N, K)
+        ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+        ws[:65536] = 0
+        C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        mx.mxfp4_gemm_ex(c.A, c.Bw, c.Bs, C, M, N, K, ws, need)
+        torch.cuda.synchronize()
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+    assert_close(bf16_dev_to_bits(C), c.ref(), sched)
+    assert int(ws[:65536].count_nonzero()) == 0  # tickets left at zero
+
+
 RAGGED_SCHEDULES = ["wide_mt4_nt7_w4_d2_split1", "wide_mt8_nt2_w8_d2_split2", "widel_mt4_nt7_w4_d3_split1"]
 
 
