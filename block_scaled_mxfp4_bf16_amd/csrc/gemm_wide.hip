@@ -218,10 +218,11 @@ __global__ __launch_bounds__(64 * W) void gemm_wide_kernel(const uint8_t *__rest
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Bw, 0, b_bytes, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Bs, 0, s_bytes, kRsrcWord3);
   // the lane's byte in a 1 KiB operand block and in a 256-byte scale block;
-  // a final half step leaves K chunks 2 and 3 of B out of range
+  // a final half step leaves K chunks 2 and 3 of B out of range (bit 31 is
+  // set with an OR, so an offset already out of range stays so)
   const int l16 = lane * 16, l4 = lane * 4;
   const int half_k = (K & 127) != 0;
-  const int l16b = (half_k && kc >= 2) ? (int)0x80000000u : l16;
+  const int half_oob = (half_k && kc >= 2) ? (int)0x80000000u : 0;
 
   struct Stage {
     u32x4 a[MW];
@@ -233,14 +234,14 @@ __global__ __launch_bounds__(64 * W) void gemm_wide_kernel(const uint8_t *__rest
   auto ring_at = [&](int d, int nt) { return wave * kWaveRing + (1 + d * NW + nt) * 1024; };
   auto load = [&](int ks, Stage &st, int d) {
     const bool ok = ks < S1;
-    const int lb = ks == KS - 1 ? l16b : l16;
+    const int lb = ks == KS - 1 ? half_oob : 0;
     if constexpr (BL) {
       // B first: the step's A (in registers) arrives after it, so waiting
       // for A also covers the ring slot
 #pragma unroll
       for (int nt = 0; nt < NW; ++nt)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (__attribute__((address_space(3))) void *)(ring + ring_at(d, nt)),
-                                                 16, uniform_off(ok, (gw + nt) * K * 8 + ks * 1024) + lb, 0, 0, 0);
+                                                 16, uniform_off(ok, (gw + nt) * K * 8 + ks * 1024 + l16) | lb, 0, 0, 0);
 #pragma unroll
       for (int q = 0; q < NSD; ++q)
         st.bs[q] = __builtin_amdgcn_raw_buffer_load_b32(
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(64 * W) void gemm_wide_kernel(const uint8_t *__rest
 #pragma unroll
       for (int nt = 0; nt < NW; ++nt)
         st.b[nt] =
-            __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, uniform_off(ok, (gw + nt) * K * 8 + ks * 1024) + lb, 0, 0);
+            __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, uniform_off(ok, (gw + nt) * K * 8 + ks * 1024 + l16) | lb, 0, 0);
 #pragma unroll
       for (int q = 0; q < NSD; ++q)
         st.bs[q] = __builtin_amdgcn_raw_buffer_load_b32(

@@ -39,8 +39,9 @@ bool g_schedule_override_set = false;
 // Schedule choice: the tuned table for the shapes measured on MI355X;
 // otherwise, for M <= 64, a search of the compiled fused kernels with
 // 16-row tiles that prefers 256-2048 workgroups, then the fewest K splits
-// across workgroups, then the least idle work per wave; for M > 64, the
-// large-M kernel whose workgroups take in the fewest bytes.
+// across workgroups, then the least idle work per wave; for M > 64, and
+// for a K too long for the fused kernels, the large-M kernel whose
+// workgroups take in the fewest bytes.
 int tiles_of(const Schedule &s, int M, int N) {
   return (N / (16 * s.nt * s.wn)) * ((M + 16 * s.mt - 1) / (16 * s.mt));
 }
@@ -85,6 +86,39 @@ const Tuned kTuned[] = {
 
 // need_pq: only schedules that read a pre-quantized A operand (for A that
 // arrives quantized).
+// The large-M kernel whose workgroups take in the fewest bytes each.  Per
+// workgroup, a K step brings 1088 bytes of A per row tile and about 1152 of
+// B per column subtile; a split adds its partial tiles; more workgroups
+// than CUs run in rounds.  It reads A quantized by its own launch, so it
+// also serves callers that need a pre-quantized schedule.
+bool pick_wide(int M, int N, int K, Schedule *out) {
+  const int ks = (K + 127) / 128;
+  bool found = false;
+  Schedule best{};
+  double best_cost = 0;
+  for (int v = 0; v < num_gemm_variants(); ++v) {
+    Schedule s;
+    gemm_variant_shape(v, &s);
+    if (s.wide != 1) continue;  // the LDS-staged variants run only when named
+    for (s.split = 1; s.split <= 8; ++s.split) {
+      if (!covers(s, M, N, K)) continue;
+      const int wgs = tiles_of(s, M, N) * s.split;
+      const double rounds = (double)((wgs + 255) / 256);
+      const double steps = (double)((ks + s.split - 1) / s.split);
+      double cost = rounds * (steps * (1.0625 * s.mt + 1.125 * s.nt) + 8.0);
+      if (s.split > 1) cost += 0.5 * s.mt * s.nt * s.split;
+      cost += 0.01 * (8 - s.wk) + 0.001 * (4 - s.kpw);  // more waves, then deeper prefetch, on a tie
+      if (!found || cost < best_cost) {
+        found = true;
+        best_cost = cost;
+        best = s;
+      }
+    }
+  }
+  if (found) *out = best;
+  return found;
+}
+
 bool pick_schedule(int M, int N, int K, Schedule *out, bool need_pq = false) {
   for (const Tuned &t : kTuned)
     if (t.M == M && t.N == N && t.K == K) {
@@ -94,39 +128,7 @@ bool pick_schedule(int M, int N, int K, Schedule *out, bool need_pq = false) {
         return true;
       }
     }
-  if (M > 64) {
-    // large M: the wide kernel whose workgroups take in the fewest bytes
-    // each.  Per workgroup, a K step brings 1088 bytes of A per row tile and
-    // about 1152 of B per column subtile; a split adds its partial tiles;
-    // more workgroups than CUs run in rounds.
-    const int ks = (K + 127) / 128;
-    bool found = false;
-    Schedule best{};
-    double best_cost = 0;
-    for (int v = 0; v < num_gemm_variants(); ++v) {
-      Schedule s;
-      gemm_variant_shape(v, &s);
-      if (s.wide != 1) continue;  // the LDS-staged variants run only when named
-      for (s.split = 1; s.split <= 8; ++s.split) {
-        if (!covers(s, M, N, K)) continue;
-        const int wgs = tiles_of(s, M, N) * s.split;
-        const double rounds = (double)((wgs + 255) / 256);
-        const double steps = (double)((ks + s.split - 1) / s.split);
-        double cost = rounds * (steps * (1.0625 * s.mt + 1.125 * s.nt) + 8.0);
-        if (s.split > 1) cost += 0.5 * s.mt * s.nt * s.split;
-        cost += 0.01 * (8 - s.wk) + 0.001 * (4 - s.kpw);  // more waves, then deeper prefetch, on a tie
-        if (!found || cost < best_cost) {
-          found = true;
-          best_cost = cost;
-          best = s;
-        }
-      }
-    }
-    if (found) {
-      *out = best;
-      return true;
-    }
-  }
+  if (M > 64 && pick_wide(M, N, K, out)) return true;
   // 16-row tiles: each workgroup then stages a quarter to a half as much A
   // as a 32- or 64-row tile would, and there are more workgroups to spread
   // B over; measured best at M = 32 and 64 as well as at M = 16
@@ -158,7 +160,9 @@ bool pick_schedule(int M, int N, int K, Schedule *out, bool need_pq = false) {
       break;  // the smallest split that covers K for this kernel
     }
   }
-  if (!found) return false;
+  // K beyond what 16 splits of any fused kernel cover: the large-M kernel
+  // loops over K
+  if (!found) return pick_wide(M, N, K, out);
   *out = best;
   return true;
 }

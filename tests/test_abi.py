@@ -246,3 +246,15 @@ def test_split_epilogue_schedule_names_cover_and_size():
     for shape in ((40, 256, 2112), (8, 2112, 7168), (16, 2112, 7168), (16, 3072, 1536), (64, 7168, 2048)):
         name = mx.mxfp4_gemm_schedule_name(*shape)
         assert "streamk" not in name and not name.endswith("_at"), (shape, name)
+
+
+def test_k_too_long_for_the_fused_kernels_goes_to_the_large_m_kernel():
+    # 16 splits of the deepest fused kernel (32 steps of 128) cover K = 65536
+    assert not mx.mxfp4_gemm_schedule_name(16, 64, 65536).startswith("wide_")
+    assert mx.mxfp4_gemm_schedule_name(16, 64, 65536 + 128).startswith("wide_")
+    for M in (1, 16, 64):
+        assert mx.mxfp4_gemm_schedule_name(M, 64, 262144).startswith("wide_")
+        assert mx.mxfp4_gemm_q_schedule_name(M, 64, 262144).startswith("wide_")
+    # the largest operands the ABI takes still have a schedule
+    assert mx.mxfp4_gemm_schedule_name(32767, 32, 32768) is not None
+    assert mx.mxfp4_gemm_schedule_name(32767, 32736, 64) is not None
