@@ -450,15 +450,26 @@ __global__ __launch_bounds__(64 * W) void gemm_wide_kernel(const uint8_t *__rest
 
   // Split K across workgroups: the same slot-and-ticket protocol as the
   // fused kernels (device-coherent slot stores, wait, ticket; the last
-  // workgroup adds the slots in split order and resets the ticket).
+  // workgroup adds the slots in split order and resets the ticket).  Slots
+  // move 16-byte chunks: buffer stores and loads with the device-coherence
+  // bit, which is what relaxed agent-scope atomic accesses compile to.
+  constexpr int kSc1 = 16;
   const int tile = m_tile * n_tiles + n_tile;
-  float *mine = partials + ((size_t)tile * split + sk) * E;
-  for (int j = threadIdx.x; j < E / 8; j += NTH) {
-    float v[8];
-    sum8(8 * j, v);
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      __hip_atomic_store(mine + 8 * j + q, v[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  auto slot_rsrc = [&](int s) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(partials + ((size_t)tile * split + s) * E), 0, E * 4,
+                                             kRsrcWord3);
+  };
+  auto as_u = [](float a, float b, float c, float d) {
+    return u32x4{__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+  };
+  {
+    const __amdgpu_buffer_rsrc_t w_rsrc = slot_rsrc(sk);
+    for (int j = threadIdx.x; j < E / 8; j += NTH) {
+      float v[8];
+      sum8(8 * j, v);
+      __builtin_amdgcn_raw_buffer_store_b128(as_u(v[0], v[1], v[2], v[3]), w_rsrc, 32 * j, 0, kSc1);
+      __builtin_amdgcn_raw_buffer_store_b128(as_u(v[4], v[5], v[6], v[7]), w_rsrc, 32 * j + 16, 0, kSc1);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -469,15 +480,19 @@ __global__ __launch_bounds__(64 * W) void gemm_wide_kernel(const uint8_t *__rest
                  : 0u;
   __syncthreads();
   if (!s_last) return;
-  const float *all = partials + (size_t)tile * split * E;
   for (int j = threadIdx.x; j < E / 8; j += NTH) {
     float v[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = 0.f;
-    for (int s = 0; s < split; ++s)
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        v[q] += __hip_atomic_load(all + (size_t)s * E + 8 * j + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int s = 0; s < split; ++s) {
+      const __amdgpu_buffer_rsrc_t r_rsrc = slot_rsrc(s);
+      const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(r_rsrc, 32 * j, 0, kSc1);
+      const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(r_rsrc, 32 * j + 16, 0, kSc1);
+      v[0] += __uint_as_float(lo.x); v[1] += __uint_as_float(lo.y);
+      v[2] += __uint_as_float(lo.z); v[3] += __uint_as_float(lo.w);
+      v[4] += __uint_as_float(hi.x); v[5] += __uint_as_float(hi.y);
+      v[6] += __uint_as_float(hi.z); v[7] += __uint_as_float(hi.w);
+    }
     store8(8 * j, v);
   }
   if (threadIdx.x == 0) __hip_atomic_store(&tickets[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
