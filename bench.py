@@ -266,9 +266,51 @@ def summarize_pmc(fetch_dir, write_dir, command):
     print(json.dumps(out))
 
 
+def expected_mfma(M, N, K):
+    """Matrix instructions the product needs at 16 x 16 x 128 per
+    instruction: 16-row tiles (rows past M padded), 16-column subtiles,
+    128-wide K steps (a final 64-wide half step counted whole)."""
+    return ((M + 15) // 16) * (N // 16) * ((K + 127) // 128)
+
+
+def summarize_mfma(pmc_dir, configs, command):
+    """Turn a rocprofv3 --pmc run (SQ_INSTS_MFMA, SQ_VALU_MFMA_BUSY_CYCLES)
+    of the bench into matrix-unit use per GEMM kernel: instructions and busy
+    SIMD cycles per dispatch (medians), the dispatch's own duration from the
+    same run, and busy cycles over what 1024 SIMDs offer in that time at the
+    nominal 2.4 GHz.  At full FP4 rate one 16x16x128 instruction keeps its
+    SIMD's matrix unit busy 16 cycles."""
+    import synthetic as syn
+    groups = {}
+    for r in _pmc_rows(pmc_dir):
+        if "gemm" not in r["Kernel_Name"]:
+            continue
+        key = (r["Kernel_Name"].split("(")[0], int(r["Grid_Size"]))
+        d = groups.setdefault(key, {})
+        disp = d.setdefault(r["Dispatch_Id"], {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        disp[r["Counter_Name"]] = float(r["Counter_Value"])
+    med = lambda v: sorted(v)[len(v) // 2]
+    want = {expected_mfma(w.M, w.N, w.K): w.name for w in (syn.CONFIGS[c] for c in configs)}
+    out = {"command": command, "kernels": []}
+    for (name, grid), d in sorted(groups.items()):
+        ds = list(d.values())
+        inst = med([x.get("SQ_INSTS_MFMA", 0.0) for x in ds])
+        busy = med([x.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for x in ds])
+        ns = med([x["ns"] for x in ds])
+        out["kernels"].append({
+            "kernel": name, "grid": grid, "dispatches": len(ds), "workload": want.get(int(inst)),
+            "mfma_instructions": int(inst), "busy_simd_cycles": int(busy),
+            "busy_cycles_per_instruction": round(busy / inst, 2) if inst else None,
+            "duration_ns": ns, "matrix_busy_frac_at_2400MHz": round(busy / (1024 * 2.4 * ns), 4) if ns else None})
+    print(json.dumps(out, indent=1))
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
         summarize_pmc(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-mfma":
+        summarize_mfma(sys.argv[2], sys.argv[3].split(","), " ".join(sys.argv[4:]))
         return
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
