@@ -438,6 +438,17 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float *__restrict__ p, in
   if (i < n4) ((v4f *)p)[i] = v4f{0.f, 0.f, 0.f, 0.f};
 }
 
+// Zero `bytes` (a multiple of 16) at a 16-byte aligned address with a fill
+// kernel rather than a memset node, which a graph capturing the call would
+// record.
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream) {
+  const size_t n4 = bytes / 16;
+  if (n4 == 0) return hipSuccess;
+  if (n4 > (size_t)INT32_MAX - 255) return hipErrorInvalidValue;
+  zero_f32_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, stream>>>((float *)p, (int)n4);
+  return hipGetLastError();
+}
+
 // A quantized once into operand blocks for the pre-quantized mode: block
 // (m tile, step) holds 1 KiB of codes (operand lane L's 16 bytes at 16*L)
 // and 64 scale bytes.  One wave per 16 rows x 32 elements, four consecutive

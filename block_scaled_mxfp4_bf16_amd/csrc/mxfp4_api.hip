@@ -258,9 +258,12 @@ struct WsEntry {
 std::mutex g_ws_mu;
 std::vector<WsEntry> g_ws;
 
+// A new buffer starts zeroed (the split-K tickets); the fill is a kernel
+// launch on `stream`, not a memset.
 mxfp4_status_t get_workspace(size_t need, hipStream_t stream, void **out) {
   *out = nullptr;
   if (need == 0) return MXFP4_OK;
+  need = (need + 255) & ~(size_t)255;
   int dev = 0;
   if (hipError_t e0 = hipGetDevice(&dev); e0 != hipSuccess) return hip_status(e0);
   std::lock_guard<std::mutex> lk(g_ws_mu);
@@ -276,7 +279,7 @@ mxfp4_status_t get_workspace(size_t need, hipStream_t stream, void **out) {
       e.ptr = nullptr;
       e.bytes = 0;
       if (hipError_t e0 = hipMalloc(&e.ptr, need); e0 != hipSuccess) return hip_status(e0);
-      if (hipError_t e0 = hipMemsetAsync(e.ptr, 0, need, stream); e0 != hipSuccess) return hip_status(e0);
+      if (hipError_t e0 = launch_zero(e.ptr, need, stream); e0 != hipSuccess) return hip_status(e0);
       e.bytes = need;
       *out = e.ptr;
       return MXFP4_OK;
@@ -284,7 +287,7 @@ mxfp4_status_t get_workspace(size_t need, hipStream_t stream, void **out) {
   }
   WsEntry e{dev, (void *)stream, nullptr, 0};
   if (hipError_t e0 = hipMalloc(&e.ptr, need); e0 != hipSuccess) return hip_status(e0);
-  if (hipError_t e0 = hipMemsetAsync(e.ptr, 0, need, stream); e0 != hipSuccess) {
+  if (hipError_t e0 = launch_zero(e.ptr, need, stream); e0 != hipSuccess) {
     (void)hipFree(e.ptr);
     return hip_status(e0);
   }

@@ -89,6 +89,7 @@ MXFP4_WIDEL_VARIANTS(MXFP4_DECLARE_WIDEL)
 
 size_t gemm_workspace_bytes(const Schedule &s, int M, int N, int K);
 hipError_t launch_gemm(const Schedule &s, const GemmArgs &a, bool sw_quant, hipStream_t stream);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);  // bytes: a multiple of 16
 
 hipError_t launch_quantize(const void *x, int64_t rows, int64_t K, void *q, void *scales, bool shuffled, bool sw,
                            hipStream_t stream);

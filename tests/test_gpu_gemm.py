@@ -340,6 +340,60 @@ def test_wide_kernel_matches_oracle(sched, M, N, K):
     assert_close(first, c.ref(), "%s %dx%dx%d" % (sched, M, N, K))
 
 
+# Calls captured into a HIP graph: the default small-M path, ticketed split K
+# (tickets must be back at zero after every replay), the float-atomic
+# epilogue (its zero fill is a kernel node), and the two-launch large-M path.
+GRAPH_CASES = [(None, 32, 4096, 512), ("mt1_nt2_wn1_wk8_kpw4_split2_r8", 8, 2112, 7168),
+               ("mt1_nt1_wn4_wk4_kpw4_split4", 16, 512, 4096), ("mt1_nt2_wn1_wk8_kpw4_split2_at", 16, 256, 7168),
+               ("wide_mt4_nt7_w4_d2_split3", 130, 448, 2112)]
+
+
+@pytest.mark.parametrize("sched,M,N,K", GRAPH_CASES)
+def test_graph_replays_match_eager(sched, M, N, K):
+    """Several calls captured in one graph, replayed four times with the
+    program's own eager work and synchronizations in between; every replay's
+    C equals the eager call's bit for bit (the atomic epilogue: within the
+    tolerance, its addition order varies) and the oracle's within tolerance."""
+    torch = torch_cuda()
+    c = make(torch, M, N, K, seed=M + K)
+    mx.mxfp4_set_schedule_override(sched)
+    try:
+        if sched is not None:
+            assert mx.mxfp4_gemm_schedule_name(M, N, K) == sched
+        stream = torch.cuda.Stream()
+        outs = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+        with torch.cuda.stream(stream):
+            mx.mxfp4_reserve(M, N, K, stream=stream)
+            mx.mxfp4_gemm(c.A, c.Bw, c.Bs, outs[0], M, N, K, stream=stream)
+        stream.synchronize()
+        eager = bf16_dev_to_bits(outs[0])
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for C in outs:
+                mx.mxfp4_gemm(c.A, c.Bw, c.Bs, C, M, N, K, stream=stream)
+        exact = sched is None or not sched.endswith("_at")
+        for rep in range(4):
+            for C in outs:
+                C.fill_(float("nan"))  # eager work between replays; a replay must overwrite all of C
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                g.replay()
+            stream.synchronize()
+            other = c.run()  # an eager call on the default stream between replays
+            for i, C in enumerate(outs):
+                got = bf16_dev_to_bits(C)
+                if exact:
+                    assert np.array_equal(got, eager), (sched, rep, i)
+                else:
+                    assert_close(got, bits_to_f64(eager), "%s replay %d call %d" % (sched, rep, i))
+            if exact:
+                assert np.array_equal(other, eager)
+        del g
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+    assert_close(eager, c.ref(), "graph case %s %dx%dx%d" % (sched, M, N, K))
+
+
 # A quantized once, handed to the GEMM: (schedule or None for the default, M, N, K)
 GEMM_Q_CASES = [("mt4_nt1_wn2_wk4_kpw4_split1_pq", 64, 7168, 2048), ("mt1_nt1_wn1_wk8_kpw4_split2_pq", 8, 2112, 7168),
                 ("mt2_nt1_wn1_wk1_kpw4_split1_pq", 32, 4096, 512), ("mt4_nt2_wn2_wk2_kpw4_split3_pq", 40, 256, 2112),
