@@ -164,8 +164,10 @@ MXFP4_API const char *mxfp4_gemm_q_schedule_name(int64_t M, int64_t N, int64_t K
 /*   C       [M, N] bf16 row-major, fully overwritten; must not alias the    */
 /*           inputs; 16-byte aligned                                (output) */
 /* mxfp4_gemm uses a library-owned workspace per (device, stream), created   */
-/* on the first call for a shape that needs more (that call allocates;       */
-/* later calls do not).  Results are deterministic: the split-K partial sums */
+/* on the first call for a shape that needs more (that call allocates and    */
+/* zeroes it with a fill kernel on `stream`, never a memset; later calls do  */
+/* not allocate).  The device is the calling thread's current device, which  */
+/* `stream` must belong to.  Results are deterministic: the split-K partial sums */
 /* are added in a fixed order (unless an "_at" schedule is forced by         */
 /* mxfp4_set_schedule_override: its float atomics add in arrival order).     */
 /* Errors: INVALID_ARG (null, M/N/K < 1, misaligned);                        */
