@@ -1,0 +1,113 @@
+"""Host-side logic of bench.py: the algorithmic byte and FLOP counts, the
+matrix-instruction count of a product, the two rocprofv3 counter summaries
+(on small synthetic counter files), and the one-GPU guard.  No GPU needed."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import synthetic as syn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size", "Kernel_Id",
+          "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count",
+          "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+
+def write_counters(d, rows):
+    """rows: (dispatch, grid, kernel, counter, value, start_ns, end_ns)"""
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "pmc_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for disp, grid, kern, ctr, val, t0, t1 in rows:
+            w.writerow({"Correlation_Id": disp, "Dispatch_Id": disp, "Agent_Id": "Agent 1", "Queue_Id": 1,
+                        "Process_Id": 1, "Thread_Id": 1, "Grid_Size": grid, "Kernel_Id": 1, "Kernel_Name": kern,
+                        "Workgroup_Size": 256, "LDS_Block_Size": 0, "Scratch_Size": 0, "VGPR_Count": 0,
+                        "Accum_VGPR_Count": 0, "SGPR_Count": 0, "Counter_Name": ctr, "Counter_Value": val,
+                        "Start_Timestamp": t0, "End_Timestamp": t1})
+
+
+def test_algorithmic_bytes_and_flops():
+    # M=32 N=4096 K=512: A bf16 + B e2m1 + B e8m0 + C bf16, each once
+    assert bench.alg_bytes(32, 4096, 512) == 2 * 32 * 512 + 4096 * 512 // 2 + 4096 * 512 // 32 + 2 * 32 * 4096
+    assert bench.alg_bytes(32, 4096, 512) == 1409024
+    assert bench.alg_flops(256, 7168, 7168) == 26306674688
+
+
+def test_expected_matrix_instructions():
+    # 16 x 16 x 128 instructions: row tiles padded to 16, half steps counted whole
+    assert bench.expected_mfma(256, 7168, 7168) == 16 * 448 * 56
+    assert bench.expected_mfma(8, 2112, 7168) == 1 * 132 * 56
+    assert bench.expected_mfma(17, 32, 192) == 2 * 2 * 2
+    for c in ("c1", "c2", "c3", "c4", "c5"):
+        w = syn.CONFIGS[c]
+        # every instruction does 2 * 16 * 16 * 128 FLOPs, padding included
+        assert bench.expected_mfma(w.M, w.N, w.K) * 65536 >= bench.alg_flops(w.M, w.N, w.K)
+
+
+def test_summarize_mfma_on_synthetic_counters(tmp_path, capsys):
+    wide = "void mxfp4::gemm_wide_kernel<4, 7, 4, 2, false>(unsigned char const*)"
+    fused = "void mxfp4::gemm_kernel<1, 1, 4, 1, 4, false, 16, 0>(unsigned short const*)"
+    quant = "mxfp4::quant_quad_kernel(unsigned short const*)"
+    rows = []
+    for i, ns in enumerate([16000, 16400, 17000]):  # median duration 16400
+        d = 10 + i
+        rows += [(d, 65536, wide, "SQ_INSTS_MFMA", 401408, 1000, 1000 + ns),
+                 (d, 65536, wide, "SQ_VALU_MFMA_BUSY_CYCLES", 401408 * 16, 1000, 1000 + ns)]
+    rows += [(20, 32768, fused, "SQ_INSTS_MFMA", 2048, 0, 4000),
+             (20, 32768, fused, "SQ_VALU_MFMA_BUSY_CYCLES", 2048 * 16, 0, 4000),
+             (21, 57344, quant, "SQ_INSTS_MFMA", 0, 0, 3000)]  # not a GEMM: ignored
+    write_counters(str(tmp_path / "pmc"), rows)
+    bench.summarize_mfma(str(tmp_path / "pmc"), ["c2", "c5"], "cmd")
+    out = json.loads(capsys.readouterr().out)
+    assert out["command"] == "cmd"
+    ks = {k["kernel"]: k for k in out["kernels"]}
+    assert set(ks) == {wide.split("(")[0], fused.split("(")[0]}
+    w = ks[wide.split("(")[0]]
+    assert w["dispatches"] == 3 and w["mfma_instructions"] == 401408
+    assert w["workload"] == syn.CONFIGS["c5"].name
+    assert w["busy_cycles_per_instruction"] == 16.0 and w["duration_ns"] == 16400
+    assert w["matrix_busy_frac_at_2400MHz"] == pytest.approx(401408 * 16 / (1024 * 2.4 * 16400), abs=1e-4)
+    assert ks[fused.split("(")[0]]["workload"] == syn.CONFIGS["c2"].name
+
+
+def test_summarize_pmc_scales_by_the_copy_calibration(tmp_path, monkeypatch, capsys):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    gemm = "void mxfp4::gemm_kernel<1, 1, 4, 1, 4, false, 16, 0>(unsigned short const*)"
+    copy = "__amd_rocclr_copyBuffer"
+    cal = bench.CALIBRATION_BYTES
+    # FETCH_SIZE reads half of a cold copy's bytes, WRITE_SIZE all of them (KiB per dispatch)
+    fetch = [(1, 1 << 20, copy, "FETCH_SIZE", 64, 0, 1), (2, 1 << 26, copy, "FETCH_SIZE", cal / 2 / 1024, 0, 1)]
+    write = [(1, 1 << 20, copy, "WRITE_SIZE", 64, 0, 1), (2, 1 << 26, copy, "WRITE_SIZE", cal / 1024, 0, 1)]
+    for i, (f, w) in enumerate([(700, 256), (720, 256), (760, 256)]):
+        fetch.append((10 + i, 32768, gemm, "FETCH_SIZE", f, 0, 1))
+        write.append((10 + i, 32768, gemm, "WRITE_SIZE", w, 0, 1))
+    write_counters(str(tmp_path / "f"), fetch)
+    write_counters(str(tmp_path / "w"), write)
+    bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), "cmd")
+    out = json.loads(capsys.readouterr().out)
+    assert out["copy_calibration"] == {"fetch": 0.5, "write": 1.0}
+    assert out["fetch_bytes_per_launch"] == 720 * 1024 * 2  # median, divided by the fetch scale
+    assert out["write_bytes_per_launch"] == 256 * 1024
+    assert out["hbm_bytes_per_launch"] == 720 * 2048 + 256 * 1024
+    assert out["gemm_dispatches"] == [3, 3]
+    with open(tmp_path / "traffic.json") as f:
+        assert json.load(f)["kernel_source_hash"] == bench.kernel_source_hash()
+    # the bench reports traffic only while the hash matches the sources
+    assert bench.measured_traffic() == out["hbm_bytes_per_launch"]
+    with open(tmp_path / "traffic.json", "w") as f:
+        json.dump(dict(out, kernel_source_hash="0" * 16), f)
+    assert bench.measured_traffic() is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 1
+    assert "one GPU" in r.stderr and r.stdout == ""
