@@ -4,11 +4,13 @@
 // Submission 711914 quantizes A with a standalone kernel when M is large
 // and hands the FP4 operands to a GEMM; this is that split, with our own
 // kernels.  The design follows from what bounds the shape on MI355X:
-//   - Each CU can take in about 64 bytes per clock through its load path.
-//     A workgroup that owns a BM x BN output tile reads (BM + BN) * K / 2
-//     bytes of codes, so the tile should be as close to square as the grid
-//     allows: at 256 x 7168 x 7168, 64 x 112 tiles make exactly 256
-//     workgroups, one per CU.
+//   - Each CU's vector cache keeps only about 64 lines (128 bytes each)
+//     outstanding to L2, and under this load a line takes ~450 cycles to
+//     arrive, so a CU's time is about (lines it requests) x 450 / 64 cycles
+//     however many loads its waves have in flight.  A workgroup that owns a
+//     BM x BN output tile requests (BM + BN) * K / 2 bytes of codes, so the
+//     tile should be as close to square as the grid allows: at 256 x 7168 x
+//     7168, 64 x 112 tiles make exactly 256 workgroups, one per CU.
 //   - Every wave holds the accumulators of the whole tile and takes every
 //     fourth 128-wide K step, loading that step's operands straight into
 //     registers three steps ahead.  No byte is loaded twice by one
