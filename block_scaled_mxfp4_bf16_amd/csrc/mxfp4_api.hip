@@ -74,7 +74,7 @@ struct Tuned {
 const Tuned kTuned[] = {
     {16, 3072, 1536, "mt1_nt2_wn1_wk8_kpw2_split1"},
     {32, 4096, 512, "mt1_nt2_wn1_wk4_kpw1_split1"},
-    {8, 2112, 7168, "mt1_nt2_wn1_wk8_kpw4_split2_r8"},
+    {8, 2112, 7168, "mt1_nt1_wn1_wk14_kpw4_split1_r8"},
     {64, 7168, 2048, "mt1_nt2_wn4_wk4_kpw4_split1"},
     {256, 7168, 7168, "wide_mt4_nt7_w4_d2_split1"},
     // the leaderboard's other shapes

@@ -74,9 +74,9 @@ def test_gemm_rejects_bad_arguments(args, code):
 
 def test_gemm_ex_rejects_small_workspace():
     L = mx.lib()
-    M, N, K = 8, 2112, 7168
+    M, N, K = 16, 2112, 7168
     need = mx.mxfp4_gemm_workspace_bytes(M, N, K)
-    assert need > 0  # long K at small M splits K over workgroups
+    assert need > 0  # long K at small M: this shape's schedule splits K over workgroups
     assert L.mxfp4_gemm_ex(FAKE, FAKE, FAKE, FAKE, M, N, K, None, 0, None) == WORKSPACE
     assert L.mxfp4_gemm_ex(FAKE, FAKE, FAKE, FAKE, M, N, K, FAKE, need - 1, None) == WORKSPACE
     assert L.mxfp4_gemm_ex(FAKE, FAKE, FAKE, FAKE, M, N, K, FAKE + 16, need, None) == WORKSPACE

@@ -154,22 +154,42 @@ def test_hw_and_sw_encoders_give_identical_c():
 
 
 def test_gemm_ex_with_caller_workspace():
+    """M=8 N=2112 K=7168 with K split over two workgroups (named: the
+    built-in choice for this shape needs no workspace)."""
     torch = torch_cuda()
     w = syn.CONFIGS["c3"]
     c = Case(torch, w.a_bits(), w.b_bits())
-    need = mx.mxfp4_gemm_workspace_bytes(c.M, c.N, c.K)
-    assert need > 0
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
-    outs = []
-    for _ in range(3):
-        C = torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")
-        mx.mxfp4_gemm_ex(c.A, c.Bw, c.Bs, C, c.M, c.N, c.K, ws, need)
-        torch.cuda.synchronize()
-        outs.append(bf16_dev_to_bits(C))
-    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
-    assert np.array_equal(outs[0], c.run())
-    # the tickets are left at zero for the next call
-    assert int(ws[:65536].count_nonzero()) == 0
+    mx.mxfp4_set_schedule_override("mt1_nt2_wn1_wk8_kpw4_split2_r8")
+    try:
+        need = mx.mxfp4_gemm_workspace_bytes(c.M, c.N, c.K)
+        assert need > 0
+        ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        outs = []
+        for _ in range(3):
+            C = torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")
+            mx.mxfp4_gemm_ex(c.A, c.Bw, c.Bs, C, c.M, c.N, c.K, ws, need)
+            torch.cuda.synchronize()
+            outs.append(bf16_dev_to_bits(C))
+        assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+        assert np.array_equal(outs[0], c.run())
+        # the tickets are left at zero for the next call
+        assert int(ws[:65536].count_nonzero()) == 0
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+    assert_close(outs[0], c.ref(), "c3 through a caller workspace")
+
+
+def test_single_split_default_needs_no_workspace():
+    """The built-in choice at M=8 N=2112 K=7168 covers K in one workgroup
+    per column tile: no workspace, and mxfp4_gemm_ex accepts none."""
+    torch = torch_cuda()
+    w = syn.CONFIGS["c3"]
+    assert mx.mxfp4_gemm_workspace_bytes(w.M, w.N, w.K) == 0
+    c = Case(torch, w.a_bits(), w.b_bits())
+    C = torch.empty((c.M, c.N), dtype=torch.bfloat16, device="cuda")
+    mx.mxfp4_gemm_ex(c.A, c.Bw, c.Bs, C, c.M, c.N, c.K, None, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_dev_to_bits(C), c.run())
 
 
 def test_reserve_then_repeated_calls_are_identical():
