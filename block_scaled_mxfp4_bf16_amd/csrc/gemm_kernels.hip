@@ -572,6 +572,9 @@ static const Variant kVariants[] = {
     V8(1, 1, 1, 16, 4), V8(1, 1, 1, 14, 4), V8(1, 1, 1, 8, 4), V8(1, 1, 1, 16, 2), V8(1, 1, 2, 8, 4), V8(1, 1, 2, 8, 2),
     V8(1, 2, 1, 16, 4), V8(1, 2, 1, 8, 4), V8(1, 1, 1, 4, 4), V8(1, 1, 1, 4, 2), V8(1, 1, 1, 8, 2), V8(1, 1, 1, 4, 1),
     V8(1, 1, 2, 4, 2), V8(1, 1, 4, 4, 4), V8(1, 1, 1, 2, 2), V8(1, 1, 1, 1, 4), V8(1, 1, 1, 2, 4),
+    // waves x steps that cover K exactly: 12 steps (K = 1536), 56 steps (K = 7168)
+    V(1, 2, 1, 12, 1), V(1, 2, 1, 6, 2), V(1, 2, 1, 4, 3), V(1, 2, 1, 3, 4), V(1, 1, 1, 12, 1), V(1, 1, 1, 6, 2),
+    V(1, 1, 2, 6, 2), V(1, 1, 1, 14, 4),
     V(1, 1, 1, 1, 1), V(1, 1, 1, 1, 2), V(1, 1, 1, 1, 4), V(1, 1, 1, 2, 1), V(1, 1, 1, 2, 2), V(1, 1, 1, 2, 4),
     V(1, 1, 1, 4, 1), V(1, 1, 1, 4, 2), V(1, 1, 1, 4, 4), V(1, 1, 1, 8, 1), V(1, 1, 1, 8, 2), V(1, 1, 1, 8, 4),
     V(1, 1, 1, 16, 1), V(1, 1, 1, 16, 2), V(1, 1, 2, 1, 1), V(1, 1, 2, 1, 2), V(1, 1, 2, 1, 4), V(1, 1, 2, 2, 1),

@@ -72,7 +72,7 @@ struct Tuned {
   const char *name;
 };
 const Tuned kTuned[] = {
-    {16, 3072, 1536, "mt1_nt2_wn1_wk8_kpw2_split1"},
+    {16, 3072, 1536, "mt1_nt2_wn1_wk4_kpw3_split1"},
     {32, 4096, 512, "mt1_nt2_wn1_wk4_kpw1_split1"},
     {8, 2112, 7168, "mt1_nt1_wn1_wk14_kpw4_split1_r8"},
     {64, 7168, 2048, "mt1_nt2_wn4_wk4_kpw4_split1"},

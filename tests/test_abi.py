@@ -249,9 +249,10 @@ def test_split_epilogue_schedule_names_cover_and_size():
 
 
 def test_k_too_long_for_the_fused_kernels_goes_to_the_large_m_kernel():
-    # 16 splits of the deepest fused kernel (32 steps of 128) cover K = 65536
-    assert not mx.mxfp4_gemm_schedule_name(16, 64, 65536).startswith("wide_")
-    assert mx.mxfp4_gemm_schedule_name(16, 64, 65536 + 128).startswith("wide_")
+    # 16 splits of the deepest 16-row fused kernel (14 waves x 4 steps of 128)
+    # cover K = 16 * 56 * 128 = 114688
+    assert not mx.mxfp4_gemm_schedule_name(16, 64, 114688).startswith("wide_")
+    assert mx.mxfp4_gemm_schedule_name(16, 64, 114688 + 128).startswith("wide_")
     for M in (1, 16, 64):
         assert mx.mxfp4_gemm_schedule_name(M, 64, 262144).startswith("wide_")
         assert mx.mxfp4_gemm_q_schedule_name(M, 64, 262144).startswith("wide_")
