@@ -575,6 +575,8 @@ static const Variant kVariants[] = {
     // waves x steps that cover K exactly: 12 steps (K = 1536), 56 steps (K = 7168)
     V(1, 2, 1, 12, 1), V(1, 2, 1, 6, 2), V(1, 2, 1, 4, 3), V(1, 2, 1, 3, 4), V(1, 1, 1, 12, 1), V(1, 1, 1, 6, 2),
     V(1, 1, 2, 6, 2), V(1, 1, 1, 14, 4),
+    // one or two waves per column group holding more columns each (K = 2048: 16 steps)
+    V(1, 4, 1, 4, 4), V(1, 8, 1, 4, 4), V(1, 4, 2, 4, 4), V(1, 4, 1, 8, 2),
     V(1, 1, 1, 1, 1), V(1, 1, 1, 1, 2), V(1, 1, 1, 1, 4), V(1, 1, 1, 2, 1), V(1, 1, 1, 2, 2), V(1, 1, 1, 2, 4),
     V(1, 1, 1, 4, 1), V(1, 1, 1, 4, 2), V(1, 1, 1, 4, 4), V(1, 1, 1, 8, 1), V(1, 1, 1, 8, 2), V(1, 1, 1, 8, 4),
     V(1, 1, 1, 16, 1), V(1, 1, 1, 16, 2), V(1, 1, 2, 1, 1), V(1, 1, 2, 1, 2), V(1, 1, 2, 1, 4), V(1, 1, 2, 2, 1),

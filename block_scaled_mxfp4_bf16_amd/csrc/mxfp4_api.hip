@@ -81,7 +81,7 @@ const Tuned kTuned[] = {
     {4, 2880, 512, "mt1_nt1_wn1_wk4_kpw1_split1_r8"},
     {16, 2112, 7168, "mt1_nt1_wn4_wk4_kpw4_split4"},
     {32, 2880, 512, "mt1_nt1_wn4_wk1_kpw4_split1"},
-    {256, 3072, 1536, "mt1_nt1_wn4_wk4_kpw4_split1"},
+    {256, 3072, 1536, "mt1_nt4_wn2_wk4_kpw4_split1"},
 };
 
 // need_pq: only schedules that read a pre-quantized A operand (for A that
