@@ -59,6 +59,7 @@ def _load():
         "mxfp4_gemm_schedule_name": (ctypes.c_char_p, [I64, I64, I64]),
         "mxfp4_set_quant_mode": (I, [I]),
         "mxfp4_set_schedule_override": (I, [ctypes.c_char_p]),
+        "mxfp4_list_schedules": (SZ, [I64, I64, I64, I, ctypes.c_char_p, SZ]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(L, name)
@@ -77,7 +78,7 @@ def exported_symbols():
     return ["mxfp4_packed_bytes", "mxfp4_raw_scale_bytes", "mxfp4_shuffled_scale_bytes",
             "mxfp4_gemm_workspace_bytes", "mxfp4_quantize", "mxfp4_preshuffle_b", "mxfp4_prepare_b", "mxfp4_gemm",
             "mxfp4_gemm_ex", "mxfp4_gemm_q", "mxfp4_gemm_q_schedule_name", "mxfp4_reserve", "mxfp4_status_string", "mxfp4_last_hip_error", "mxfp4_gemm_schedule_name",
-            "mxfp4_set_quant_mode", "mxfp4_set_schedule_override"]
+            "mxfp4_set_quant_mode", "mxfp4_set_schedule_override", "mxfp4_list_schedules"]
 
 
 def _check(rc: int, what: str):
@@ -175,6 +176,18 @@ def mxfp4_set_quant_mode(mode: int):
 
 def mxfp4_set_schedule_override(name):
     _check(_load().mxfp4_set_schedule_override(name.encode() if name else None), "mxfp4_set_schedule_override")
+
+
+def mxfp4_list_schedules(M: int, N: int, K: int, quantized_a: bool = False):
+    """Names of every compiled schedule that can serve (M, N, K) (empty for a
+    shape outside the ABI); each is accepted by mxfp4_set_schedule_override."""
+    L = _load()
+    need = L.mxfp4_list_schedules(M, N, K, int(quantized_a), None, 0)
+    if need == 0:
+        return []
+    buf = ctypes.create_string_buffer(need + 1)
+    L.mxfp4_list_schedules(M, N, K, int(quantized_a), buf, need + 1)
+    return buf.value.decode().split()
 
 
 # ---- tensor conveniences (allocate outputs with torch, then call the above) --

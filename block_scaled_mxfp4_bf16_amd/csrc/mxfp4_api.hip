@@ -471,6 +471,43 @@ const char *mxfp4_gemm_q_schedule_name(int64_t M, int64_t N, int64_t K) {
   return buf;
 }
 
+size_t mxfp4_list_schedules(int64_t M, int64_t N, int64_t K, int quantized_a, char *buf, size_t cap) {
+  if (cap > 0 && buf) buf[0] = 0;
+  if (M < 1 || N < 1 || K < 64 || K % 64 != 0 || N % 32 != 0) return 0;
+  if (M * K * 2 >= kMaxBytes || N * K / 2 >= kMaxBytes || M * N * 2 >= kMaxBytes ||
+      pad_to(N, 256) * pad_to(K / 32, 8) >= kMaxBytes)
+    return 0;
+  std::string out;
+  char name[96];
+  auto add = [&](const Schedule &s) {
+    schedule_to_name(s, name, sizeof(name));
+    out += name;
+    out += '\n';
+  };
+  const bool q = quantized_a != 0;
+  const int ks = (int)((K + 127) / 128);  // a split beyond this leaves workgroups without a step
+  for (int v = 0; v < num_gemm_variants(); ++v) {  // fused kernels, ticketed epilogue
+    Schedule s;
+    gemm_variant_shape(v, &s);
+    if (s.wide || s.epi || s.pq != (q ? 1 : 0)) continue;
+    for (s.split = 1; s.split <= 16 && s.split <= ks; ++s.split)
+      if (covers(s, (int)M, (int)N, (int)K)) add(s);
+  }
+  for (int v = 0; v < num_gemm_variants(); ++v) {  // large-M kernels
+    Schedule s;
+    gemm_variant_shape(v, &s);
+    if (!s.wide) continue;
+    for (s.split = 1; s.split <= 8 && s.split <= ks; ++s.split)
+      if (covers(s, (int)M, (int)N, (int)K)) add(s);
+  }
+  if (cap > 0 && buf) {
+    const size_t n = out.size() < cap - 1 ? out.size() : cap - 1;
+    memcpy(buf, out.data(), n);
+    buf[n] = 0;
+  }
+  return out.size();
+}
+
 mxfp4_status_t mxfp4_reserve(int64_t M, int64_t N, int64_t K, mxfp4_stream_t stream) {
   if (M < 1 || N < 1 || K < 1) return MXFP4_ERR_INVALID_ARG;
   if (K % 64 != 0 || N % 32 != 0) return MXFP4_ERR_UNSUPPORTED;

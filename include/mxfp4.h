@@ -231,6 +231,19 @@ MXFP4_API mxfp4_status_t mxfp4_set_quant_mode(int mode);
  * Errors: INVALID_ARG for a name no compiled kernel matches. */
 MXFP4_API mxfp4_status_t mxfp4_set_schedule_override(const char *name);
 
+/* Tuning: the names of every compiled schedule that can serve (M, N, K),
+ * one per line, for timing with mxfp4_set_schedule_override.  Listed: the
+ * fused kernels with the ticketed split epilogue at each split 1..16 that
+ * covers K (for quantized_a != 0, the ones that read A as codes, as
+ * mxfp4_gemm_q does), then the large-M kernels at splits 1..8; no split
+ * larger than K's count of 128-wide steps.  The
+ * built-in choice is always among them.  Host-only; no GPU needed.
+ * Writes at most `cap` bytes into `buf`, always NUL-terminated when
+ * cap > 0 (names are cut only at the cap), and returns the length the whole
+ * list needs, without the NUL: call once with cap = 0 to size the buffer.
+ * Returns 0 for a shape outside the ABI (see mxfp4_gemm's errors). */
+MXFP4_API size_t mxfp4_list_schedules(int64_t M, int64_t N, int64_t K, int quantized_a, char *buf, size_t cap);
+
 #ifdef __cplusplus
 }
 #endif

@@ -259,3 +259,35 @@ def test_k_too_long_for_the_fused_kernels_goes_to_the_large_m_kernel():
     # the largest operands the ABI takes still have a schedule
     assert mx.mxfp4_gemm_schedule_name(32767, 32, 32768) is not None
     assert mx.mxfp4_gemm_schedule_name(32767, 32736, 64) is not None
+
+
+@pytest.mark.parametrize("M,N,K,q", [(32, 4096, 512, False), (8, 2112, 7168, False), (256, 7168, 7168, False),
+                                     (100, 224, 2112, False), (32, 4096, 512, True), (1, 64, 64, False)])
+def test_listed_schedules_round_trip_and_include_the_builtin(M, N, K, q):
+    names = mx.mxfp4_list_schedules(M, N, K, q)
+    assert names and len(names) == len(set(names))
+    builtin = (mx.mxfp4_gemm_q_schedule_name if q else mx.mxfp4_gemm_schedule_name)(M, N, K)
+    assert builtin in names
+    ks = (K + 127) // 128
+    step = max(1, len(names) // 60)  # a spread of them: each is accepted and serves the shape as named
+    try:
+        for n in names[::step] + names[-3:]:
+            assert int(n.rsplit("split", 1)[1].split("_")[0]) <= ks
+            mx.mxfp4_set_schedule_override(n)
+            assert (mx.mxfp4_gemm_q_schedule_name if q else mx.mxfp4_gemm_schedule_name)(M, N, K) == n
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+
+
+def test_list_schedules_sizing_and_rejected_shapes():
+    L = mx.lib()
+    need = L.mxfp4_list_schedules(16, 3072, 1536, 0, None, 0)
+    full = ctypes.create_string_buffer(need + 1)
+    assert L.mxfp4_list_schedules(16, 3072, 1536, 0, full, need + 1) == need
+    assert len(full.value) == need and full.value.endswith(b"\n")
+    small = ctypes.create_string_buffer(11)
+    assert L.mxfp4_list_schedules(16, 3072, 1536, 0, small, 11) == need
+    assert small.value == full.value[:10]  # cut at the cap, NUL-terminated
+    for shape in ((0, 64, 64), (16, 48, 64), (16, 64, 96), (16, 64, 0)):
+        assert L.mxfp4_list_schedules(*shape, 0, None, 0) == 0
+        assert mx.mxfp4_list_schedules(*shape) == []

@@ -477,3 +477,16 @@ def test_default_schedules_match_oracle(M, N, K):
     mx.mxfp4_gemm_ex(c.A, c.Bw, c.Bs, C, M, N, K, ws if need else None, need)
     torch.cuda.synchronize()
     assert np.array_equal(bf16_dev_to_bits(C), c.run())
+
+
+def test_tuner_times_every_listed_schedule():
+    """The tuning module on a small shape: every listed schedule is timed,
+    the finalists include the built-in choice, and the best one is listed."""
+    torch_cuda()
+    from block_scaled_mxfp4_bf16_amd import tune
+    res = tune.tune(16, 256, 512, steps=10, top=2, confirm=1, log=lambda s: None)
+    names = mx.mxfp4_list_schedules(16, 256, 512)
+    assert set(res["times_us"]) == set(names)
+    assert all(t > 0 for t in res["times_us"].values())
+    assert res["builtin"] in res["confirmed_us"] and res["best"] in names
+    assert mx.mxfp4_gemm_schedule_name(16, 256, 512) == res["builtin"]  # the override is cleared afterwards
