@@ -84,42 +84,50 @@ const Tuned kTuned[] = {
     {256, 3072, 1536, "mt1_nt4_wn2_wk4_kpw4_split1"},
 };
 
-// need_pq: only schedules that read a pre-quantized A operand (for A that
-// arrives quantized).
-// The large-M kernel whose workgroups take in the fewest bytes each.  Per
-// workgroup, a K step brings 1088 bytes of A per row tile and about 1152 of
-// B per column subtile; a split adds its partial tiles; more workgroups
-// than CUs run in rounds.  It reads A quantized by its own launch, so it
-// also serves callers that need a pre-quantized schedule.
-bool pick_wide(int M, int N, int K, Schedule *out) {
+// Estimated cost of a large-M schedule, in log-microseconds on the same
+// scale as fused_cost: lines per CU as there (A as codes, quantized by the
+// launch before; B codes and scales), and a split of K across workgroups.
+// Fitted like fused_cost, to every large-M schedule of eight shapes with
+// M 96-256 (N 2048-14336, K 1024-14336).
+double wide_cost(const Schedule &s, int M, int N, int K) {
   const int ks = (K + 127) / 128;
+  const int per = (ks + s.split - 1) / s.split;
+  const double rows = 16.0 * s.mt, cols = 16.0 * s.nt;
+  const double wgs = (double)tiles_of(s, M, N) * s.split;
+  const double lines = (rows + cols) * per * 0.5 + rows / 64.0 * per * 2.0 + cols / 32.0 * per * 2.0;
+  return 2.226 + 1.2177e-4 * std::ceil(wgs / 256.0) * lines + (s.split > 1 ? 1.012 : 0.0);
+}
+
+// The large-M schedule of least estimated cost (B in registers; the
+// LDS-staged variants run only when named); on equal cost, fewer waves.
+// It reads A quantized by its own launch, so it also serves callers that
+// need a pre-quantized schedule.
+bool pick_wide(int M, int N, int K, Schedule *out, double *cost_out = nullptr) {
   bool found = false;
   Schedule best{};
   double best_cost = 0;
   for (int v = 0; v < num_gemm_variants(); ++v) {
     Schedule s;
     gemm_variant_shape(v, &s);
-    if (s.wide != 1) continue;  // the LDS-staged variants run only when named
+    if (s.wide != 1) continue;
     for (s.split = 1; s.split <= 8; ++s.split) {
       if (!covers(s, M, N, K)) continue;
-      const int wgs = tiles_of(s, M, N) * s.split;
-      const double rounds = (double)((wgs + 255) / 256);
-      const double steps = (double)((ks + s.split - 1) / s.split);
-      double cost = rounds * (steps * (1.0625 * s.mt + 1.125 * s.nt) + 8.0);
-      if (s.split > 1) cost += 0.5 * s.mt * s.nt * s.split;
-      cost += 0.01 * (8 - s.wk) + 0.001 * (4 - s.kpw);  // more waves, then deeper prefetch, on a tie
-      if (!found || cost < best_cost) {
+      const double cost = wide_cost(s, M, N, K);
+      if (!found || cost < best_cost - 1e-12 || (cost < best_cost + 1e-12 && s.wk < best.wk)) {
         found = true;
         best_cost = cost;
         best = s;
       }
     }
   }
-  if (found) *out = best;
+  if (found) {
+    *out = best;
+    if (cost_out) *cost_out = best_cost;
+  }
   return found;
 }
 
-// Estimated cost of a fused schedule, in log-microseconds up to a constant.
+// Estimated cost of a fused schedule, in log-microseconds.
 // A CU keeps only ~64 lines (128 bytes) outstanding to L2, so a workgroup's
 // time grows with the lines it requests: A rows actually present (bf16, or
 // codes when A arrives quantized), B columns and B scales, over its K run;
@@ -138,7 +146,7 @@ double fused_cost(const Schedule &s, int M, int N, int K, bool quantized_a, doub
   const double lines = a_lines + cols * per * 0.5 + cols / 32.0 * per * 2.0;
   const double per_cu = std::ceil(wgs / 256.0) * lines;
   *pad = (double)(s.wk * s.kpw - per) / (s.wk * s.kpw);
-  return 1.215e-4 * per_cu + 0.02547 * s.split + (s.split > 1 ? 0.1405 : 0.0);
+  return 1.978 + 1.215e-4 * per_cu + 0.02547 * s.split + (s.split > 1 ? 0.1405 : 0.0);
 }
 
 bool pick_schedule(int M, int N, int K, Schedule *out, bool need_pq = false) {
@@ -150,7 +158,6 @@ bool pick_schedule(int M, int N, int K, Schedule *out, bool need_pq = false) {
         return true;
       }
     }
-  if (M > 64 && pick_wide(M, N, K, out)) return true;
   // 16-row tiles: each workgroup then stages a quarter to a half as much A
   // as a 32- or 64-row tile would, and there are more workgroups to spread
   // B over; measured best at M = 32 and 64 as well as at M = 16
@@ -179,9 +186,16 @@ bool pick_schedule(int M, int N, int K, Schedule *out, bool need_pq = false) {
       }
     }
   }
-  // K beyond what 16 splits of any fused kernel cover: the large-M kernel
-  // loops over K
-  if (!found) return pick_wide(M, N, K, out);
+  // Above 64 rows the large-M kernel competes on estimated time (it wins
+  // unless K is short); K beyond what 16 splits of any fused kernel cover
+  // goes to it as well, since it loops over K.
+  Schedule w;
+  double w_cost = 0;
+  if ((M > 64 || !found) && pick_wide(M, N, K, &w, &w_cost) && (!found || w_cost < best_cost)) {
+    *out = w;
+    return true;
+  }
+  if (!found) return false;
   *out = best;
   return true;
 }

@@ -90,7 +90,11 @@ def tune(M, N, K, quantized_a=False, steps=200, top=10, confirm=3, log=print):
     builtin = (mx.mxfp4_gemm_q_schedule_name if quantized_a else mx.mxfp4_gemm_schedule_name)(M, N, K)
     bufs = prepare(M, N, K, quantized_a)
     stream = torch.cuda.Stream()
-    times = {n: time_schedule(M, N, K, quantized_a, bufs, stream, n, steps) for n in names}
+    times = {}
+    for i, n in enumerate(names):
+        times[n] = time_schedule(M, N, K, quantized_a, bufs, stream, n, steps)
+        if (i + 1) % 100 == 0:
+            log("  %dx%dx%d: %d of %d schedules timed" % (M, N, K, i + 1, len(names)))
     ranked = sorted(times, key=times.get)
     finalists = ranked[:top] + ([builtin] if builtin not in ranked[:top] else [])
     again = {n: [] for n in finalists}

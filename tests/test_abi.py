@@ -291,3 +291,15 @@ def test_list_schedules_sizing_and_rejected_shapes():
     for shape in ((0, 64, 64), (16, 48, 64), (16, 64, 96), (16, 64, 0)):
         assert L.mxfp4_list_schedules(*shape, 0, None, 0) == 0
         assert mx.mxfp4_list_schedules(*shape) == []
+
+
+def test_above_64_rows_the_choice_compares_kernel_families():
+    # the large-M kernel wins on long enough K and wide N; a fused kernel on short K or narrow N
+    assert mx.mxfp4_gemm_schedule_name(160, 4096, 2048).startswith("wide_")
+    assert mx.mxfp4_gemm_schedule_name(128, 14336, 4096) == "wide_mt4_nt7_w4_d2_split1"
+    assert not mx.mxfp4_gemm_schedule_name(129, 3584, 2048).startswith("wide")
+    assert not mx.mxfp4_gemm_schedule_name(160, 5120, 1024).startswith("wide")
+    # the large-M kernel does not split K across workgroups unless K is beyond the fused kernels
+    for M, N, K in ((96, 7168, 2048), (192, 2048, 7168), (256, 4096, 4096), (128, 4096, 14336)):
+        name = mx.mxfp4_gemm_schedule_name(M, N, K)
+        assert not name.startswith("wide") or name.endswith("_split1"), name

@@ -459,7 +459,10 @@ def test_gemm_q_default_schedule_on_oracle_quantized_a(name):
 # Shapes outside the tuned table: the default schedule choice for small,
 # ragged and large M, long and half-step K, narrow and odd-tile N.
 DEFAULT_SHAPES = [(1, 32, 64), (3, 96, 4160), (17, 288, 448), (48, 1024, 1024), (65, 96, 192), (100, 224, 2112),
-                  (300, 64, 1088), (513, 288, 640), (64, 32, 8192)]
+                  (300, 64, 1088), (513, 288, 640), (64, 32, 8192),
+                  # above 64 rows the estimated-time choice between the kernel families: the
+                  # large-M kernel here, a fused one (ragged M) next
+                  (160, 4096, 2048), (129, 3584, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", DEFAULT_SHAPES)
