@@ -204,7 +204,11 @@ MXFP4_API const char *mxfp4_last_hip_error(void);
  * storage, valid until the next call on the thread), e.g.
  * "mt1_nt1_wn2_wk4_kpw1_split2" (16-row M tiles, 16-column subtiles per
  * wave, waves along N, waves along K, K steps per wave, workgroups per
- * output tile along K); NULL if the shape is unsupported. */
+ * output tile along K); NULL if the shape is unsupported.  The choice: the
+ * measured best for the shapes of a built-in table, else the least
+ * estimated time among the compiled fused kernels (and, above 64 rows or
+ * for K too long for them, the large-M kernels), the estimate growing with
+ * the 128-byte lines each CU must request. */
 MXFP4_API const char *mxfp4_gemm_schedule_name(int64_t M, int64_t N, int64_t K);
 
 /* Process-wide choice of the e2m1 encoder used by mxfp4_quantize and the
