@@ -577,6 +577,7 @@ static const Variant kVariants[] = {
     V(1, 1, 2, 6, 2), V(1, 1, 1, 14, 4),
     // one or two waves per column group holding more columns each (K = 2048: 16 steps)
     V(1, 4, 1, 4, 4), V(1, 8, 1, 4, 4), V(1, 4, 2, 4, 4), V(1, 4, 1, 8, 2),
+    V(1, 2, 8, 2, 8),  // 16 x 256 tiles, 16 waves of 8 steps (256 x 3072 x 1536)
     V(1, 1, 1, 1, 1), V(1, 1, 1, 1, 2), V(1, 1, 1, 1, 4), V(1, 1, 1, 2, 1), V(1, 1, 1, 2, 2), V(1, 1, 1, 2, 4),
     V(1, 1, 1, 4, 1), V(1, 1, 1, 4, 2), V(1, 1, 1, 4, 4), V(1, 1, 1, 8, 1), V(1, 1, 1, 8, 2), V(1, 1, 1, 8, 4),
     V(1, 1, 1, 16, 1), V(1, 1, 1, 16, 2), V(1, 1, 2, 1, 1), V(1, 1, 2, 1, 2), V(1, 1, 2, 1, 4), V(1, 1, 2, 2, 1),
