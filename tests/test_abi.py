@@ -299,6 +299,9 @@ def test_above_64_rows_the_choice_compares_kernel_families():
     assert mx.mxfp4_gemm_schedule_name(128, 14336, 4096) == "wide_mt4_nt7_w4_d2_split1"
     assert not mx.mxfp4_gemm_schedule_name(129, 3584, 2048).startswith("wide")
     assert not mx.mxfp4_gemm_schedule_name(160, 5120, 1024).startswith("wide")
+    # below 64 rows it competes too: long K and wide N
+    assert mx.mxfp4_gemm_schedule_name(64, 4096, 14336).startswith("wide_")
+    assert not mx.mxfp4_gemm_schedule_name(16, 4096, 14336).startswith("wide")
     # the large-M kernel does not split K across workgroups unless K is beyond the fused kernels
     for M, N, K in ((96, 7168, 2048), (192, 2048, 7168), (256, 4096, 4096), (128, 4096, 14336)):
         name = mx.mxfp4_gemm_schedule_name(M, N, K)

@@ -493,3 +493,18 @@ def test_tuner_times_every_listed_schedule():
     assert all(t > 0 for t in res["times_us"].values())
     assert res["builtin"] in res["confirmed_us"] and res["best"] in names
     assert mx.mxfp4_gemm_schedule_name(16, 256, 512) == res["builtin"]  # the override is cleared afterwards
+
+
+def test_long_k_at_few_rows_uses_the_large_m_kernel_sampled():
+    """M=40 N=3584 K=14336: the estimated-time choice takes the large-M
+    kernel below 64 rows when K is long and N wide; sampled outputs against
+    the oracle one by one, every row tile and a spread of columns."""
+    torch = torch_cuda()
+    M, N, K = 40, 3584, 14336
+    assert mx.mxfp4_gemm_schedule_name(M, N, K).startswith("wide_")
+    c = make(torch, M, N, K, seed=77)
+    got = c.run()
+    rng = np.random.default_rng(7)
+    ms = np.concatenate([np.arange(M), rng.integers(0, M, 1200)])
+    ns = np.concatenate([rng.integers(0, N, M), rng.integers(0, N, 1200)])
+    assert_close(got[ms, ns], c.ref_sampled(ms, ns), "40x3584x14336 sampled")
