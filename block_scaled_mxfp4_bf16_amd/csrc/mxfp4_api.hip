@@ -170,14 +170,15 @@ bool pick_schedule(int M, int N, int K, Schedule *out, bool need_pq = false) {
     gemm_variant_shape(v, &s);
     if (s.mt != mt || s.pq != (need_pq ? 1 : 0) || s.wide || s.epi) continue;  // atomic and stream-K: named only
     if (!need_pq && (s.rb == 8) != (M <= 8)) continue;
-    // eight waves across 256 columns: the estimate overrates these wide tiles at
-    // short K (measured 38 % slower than the pick without them at 160 x 5120 x
-    // 1024), so they run only where the tuned table names them
-    if (s.wn >= 8) continue;
     for (s.split = 1; s.split <= 16; ++s.split) {
       if (!covers(s, M, N, K)) continue;
       double pad = 0;
       const double cost = fused_cost(s, M, N, K, need_pq, &pad);
+      // eight waves across 256 columns: measured the best where their steps
+      // cover the workgroup's K run exactly (32 x 8192 x 8192: 13.6 against
+      // 20.5 us), but the estimate overrates them with idle steps (160 x 5120 x
+      // 1024: 7.8 against 5.6 us), so only exact covers are offered
+      if (s.wn >= 8 && pad > 0) continue;
       // equal cost: the least idle K capacity, then the most waves
       const bool better = !found || cost < best_cost - 1e-12 ||
                           (cost < best_cost + 1e-12 &&

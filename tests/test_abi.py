@@ -295,10 +295,14 @@ def test_list_schedules_sizing_and_rejected_shapes():
 
 def test_above_64_rows_the_choice_compares_kernel_families():
     # the large-M kernel wins on long enough K and wide N; a fused kernel on short K or narrow N
-    assert mx.mxfp4_gemm_schedule_name(160, 4096, 2048).startswith("wide_")
+    assert mx.mxfp4_gemm_schedule_name(192, 2048, 4096).startswith("wide_")
     assert mx.mxfp4_gemm_schedule_name(128, 14336, 4096) == "wide_mt4_nt7_w4_d2_split1"
     assert not mx.mxfp4_gemm_schedule_name(129, 3584, 2048).startswith("wide")
     assert not mx.mxfp4_gemm_schedule_name(160, 5120, 1024).startswith("wide")
+    # 256-column fused tiles only where their steps cover K exactly
+    assert mx.mxfp4_gemm_schedule_name(32, 8192, 8192) == "mt1_nt2_wn8_wk2_kpw8_split4"
+    assert "_wn8_" not in mx.mxfp4_gemm_schedule_name(160, 5120, 1024)
+    assert "_wn8_" not in mx.mxfp4_gemm_schedule_name(64, 4096, 14336)
     # below 64 rows it competes too: long K and wide N
     assert mx.mxfp4_gemm_schedule_name(64, 4096, 14336).startswith("wide_")
     assert not mx.mxfp4_gemm_schedule_name(16, 4096, 14336).startswith("wide")

@@ -461,8 +461,8 @@ def test_gemm_q_default_schedule_on_oracle_quantized_a(name):
 DEFAULT_SHAPES = [(1, 32, 64), (3, 96, 4160), (17, 288, 448), (48, 1024, 1024), (65, 96, 192), (100, 224, 2112),
                   (300, 64, 1088), (513, 288, 640), (64, 32, 8192),
                   # above 64 rows the estimated-time choice between the kernel families: the
-                  # large-M kernel here, a fused one (ragged M) next
-                  (160, 4096, 2048), (129, 3584, 2048)]
+                  # large-M kernel, a fused one (ragged M), 256-column fused tiles
+                  (192, 2048, 4096), (129, 3584, 2048), (160, 4096, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", DEFAULT_SHAPES)
