@@ -5,7 +5,9 @@
 #include <string.h>
 
 #include <cmath>
+#include <map>
 #include <mutex>
+#include <tuple>
 #include <string>
 #include <vector>
 
@@ -266,13 +268,41 @@ void schedule_to_name(const Schedule &s, char *buf, size_t n) {
              s.epi == 1 ? "_at" : "");
 }
 
+// The built-in choice depends only on the shape, the form of A and the
+// compiled tables, so it is made once per shape: the search costs several
+// microseconds of host time, a lookup well under one.  Bounded: the memo is
+// emptied when it holds 4096 shapes.
+struct ChoiceMemo {
+  bool ok;
+  Schedule s;
+};
+std::mutex g_memo_mu;
+std::map<std::tuple<int, int, int, bool>, ChoiceMemo> g_memo;
+
 bool choose(int M, int N, int K, Schedule *s, bool need_pq = false) {
   {
     std::lock_guard<std::mutex> lk(g_opt_mu);
     if (g_schedule_override_set)
       return parse_schedule(g_schedule_override, M, N, K, s) && (s->pq || !need_pq);
   }
-  return pick_schedule(M, N, K, s, need_pq);
+  const auto key = std::make_tuple(M, N, K, need_pq);
+  {
+    std::lock_guard<std::mutex> lk(g_memo_mu);
+    const auto it = g_memo.find(key);
+    if (it != g_memo.end()) {
+      if (it->second.ok) *s = it->second.s;
+      return it->second.ok;
+    }
+  }
+  Schedule r{};
+  const bool ok = pick_schedule(M, N, K, &r, need_pq);
+  {
+    std::lock_guard<std::mutex> lk(g_memo_mu);
+    if (g_memo.size() >= 4096) g_memo.clear();
+    g_memo[key] = ChoiceMemo{ok, r};
+  }
+  if (ok) *s = r;
+  return ok;
 }
 
 mxfp4_status_t check_gemm_args(const void *A, const void *Bq, const void *Bs, const void *C, int64_t M, int64_t N,
