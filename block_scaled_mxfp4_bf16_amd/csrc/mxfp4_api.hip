@@ -7,8 +7,8 @@
 #include <cmath>
 #include <map>
 #include <mutex>
-#include <tuple>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "../../include/mxfp4.h"
@@ -40,10 +40,10 @@ std::string g_schedule_override;
 bool g_schedule_override_set = false;
 
 // Schedule choice: the tuned table for the shapes measured on MI355X;
-// otherwise, for M <= 64, a search of the compiled fused kernels with
-// 16-row tiles by an estimated cost (fused_cost below); for M > 64, and for
-// a K too long for the fused kernels, the large-M kernel whose workgroups
-// take in the fewest bytes.
+// otherwise the compiled schedule of least estimated time -- the fused
+// kernels with 16-row tiles (fused_cost) against the large-M kernels
+// (wide_cost), the large-M kernels alone when K is too long for the fused
+// ones.  The choice is remembered per shape (choose).
 int tiles_of(const Schedule &s, int M, int N) {
   return (N / (16 * s.nt * s.wn)) * ((M + 16 * s.mt - 1) / (16 * s.mt));
 }
