@@ -508,3 +508,15 @@ def test_long_k_at_few_rows_uses_the_large_m_kernel_sampled():
     ms = np.concatenate([np.arange(M), rng.integers(0, M, 1200)])
     ns = np.concatenate([rng.integers(0, N, M), rng.integers(0, N, 1200)])
     assert_close(got[ms, ns], c.ref_sampled(ms, ns), "40x3584x14336 sampled")
+
+
+def test_tuner_with_quantized_a():
+    """The tuning module in its pre-quantized-A mode (mxfp4_gemm_q): every
+    listed pre-quantized schedule is timed and the built-in one is among the
+    finalists."""
+    torch_cuda()
+    from block_scaled_mxfp4_bf16_amd import tune
+    res = tune.tune(32, 256, 1024, quantized_a=True, steps=10, top=1, confirm=1, log=lambda s: None)
+    assert set(res["times_us"]) == set(mx.mxfp4_list_schedules(32, 256, 1024, True))
+    assert res["builtin"] == mx.mxfp4_gemm_q_schedule_name(32, 256, 1024)
+    assert res["builtin"] in res["confirmed_us"]
