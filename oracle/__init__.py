@@ -3,8 +3,9 @@
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package; the product path never does.  It
 shares no code with the HIP library.  The arithmetic lives in
-``mxfp4_oracle.c`` (plain C, exact integer quantization, fp64 GEMM); this
-module only marshals numpy arrays through ctypes.
+``mxfp4_oracle.c`` (plain C, exact integer quantization, a GEMM in fp64 and
+in fp32 group accumulation, OpenMP over independent outputs); this module
+only marshals numpy arrays through ctypes.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed
 forms, exhaustive brute force, page constants and library special cases.
@@ -27,7 +28,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(
-            ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+            ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
              "-fvisibility=hidden", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
@@ -48,18 +49,16 @@ def lib():
         L.oracle_e2m1_value.argtypes = [ctypes.c_int]
         L.oracle_e8m0_value.restype = ctypes.c_double
         L.oracle_e8m0_value.argtypes = [ctypes.c_int]
-        L.oracle_bf16_value.restype = ctypes.c_double
-        L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
         L.oracle_scale_byte.restype = ctypes.c_int
         L.oracle_scale_byte.argtypes = [P, ctypes.c_int]
         L.oracle_encode.restype = ctypes.c_int
         L.oracle_encode.argtypes = [ctypes.c_uint16, ctypes.c_int]
-        L.oracle_encode_bittrick.restype = ctypes.c_int
-        L.oracle_encode_bittrick.argtypes = [ctypes.c_uint16, ctypes.c_int]
+        L.oracle_encode_nearest.restype = ctypes.c_int
+        L.oracle_encode_nearest.argtypes = [ctypes.c_uint16, ctypes.c_int]
         L.oracle_encode_many.restype = None
         L.oracle_encode_many.argtypes = [P, P, I64, P]
-        L.oracle_encode_bittrick_many.restype = None
-        L.oracle_encode_bittrick_many.argtypes = [P, P, I64, P]
+        L.oracle_encode_nearest_many.restype = None
+        L.oracle_encode_nearest_many.argtypes = [P, P, I64, P]
         L.oracle_quantize.restype = ctypes.c_int
         L.oracle_quantize.argtypes = [P, I64, I64, P, P]
         L.oracle_dequantize.restype = None
@@ -76,6 +75,10 @@ def lib():
         L.oracle_unpreshuffle_b.argtypes = [P, I64, I64, P]
         L.oracle_gemm_f64.restype = None
         L.oracle_gemm_f64.argtypes = [P, P, P, P, I64, I64, I64, P]
+        L.oracle_gemm_f32.restype = None
+        L.oracle_gemm_f32.argtypes = [P, P, P, P, I64, I64, I64, P]
+        L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_num_threads.argtypes = []
         L.oracle_gemm_f64_sampled.restype = None
         L.oracle_gemm_f64_sampled.argtypes = [P, P, P, P, I64, I64, I64, P, P, I64, P]
         L.oracle_bf16_from_f64.restype = ctypes.c_uint16
@@ -83,7 +86,7 @@ def lib():
         L.oracle_bf16_from_f64_many.restype = None
         L.oracle_bf16_from_f64_many.argtypes = [P, I64, P]
         L.oracle_mxfp4_gemm_bf16.restype = ctypes.c_int
-        L.oracle_mxfp4_gemm_bf16.argtypes = [P, P, P, I64, I64, I64, P]
+        L.oracle_mxfp4_gemm_bf16.argtypes = [P, P, P, I64, I64, I64, P, ctypes.c_int]
         _lib = L
     return _lib
 
@@ -109,10 +112,6 @@ def e8m0_value(b: int) -> float:
     return lib().oracle_e8m0_value(int(b))
 
 
-def bf16_value(h: int) -> float:
-    return lib().oracle_bf16_value(int(h))
-
-
 def scale_byte(group_bits) -> int:
     g = _u16(group_bits)
     return lib().oracle_scale_byte(_p(g), int(g.size))
@@ -122,8 +121,8 @@ def encode(x_bits: int, s: int) -> int:
     return lib().oracle_encode(int(x_bits), int(s))
 
 
-def encode_bittrick(x_bits: int, s: int) -> int:
-    return lib().oracle_encode_bittrick(int(x_bits), int(s))
+def encode_nearest(x_bits: int, s: int) -> int:
+    return lib().oracle_encode_nearest(int(x_bits), int(s))
 
 
 def encode_many(x_bits, s) -> np.ndarray:
@@ -134,11 +133,11 @@ def encode_many(x_bits, s) -> np.ndarray:
     return out
 
 
-def encode_bittrick_many(x_bits, s) -> np.ndarray:
+def encode_nearest_many(x_bits, s) -> np.ndarray:
     x = _u16(x_bits).ravel()
     sc = np.ascontiguousarray(np.broadcast_to(np.asarray(s, dtype=np.uint8), x.shape))
     out = np.empty(x.shape, dtype=np.uint8)
-    lib().oracle_encode_bittrick_many(_p(x), _p(sc), x.size, _p(out))
+    lib().oracle_encode_nearest_many(_p(x), _p(sc), x.size, _p(out))
     return out
 
 
@@ -215,6 +214,25 @@ def gemm_f64(qa, sa, qb, sb) -> np.ndarray:
     return C
 
 
+def gemm_f32(qa, sa, qb, sb) -> np.ndarray:
+    """C = deq(A) @ deq(B)^T with the matrix unit's accumulation: per 32-group
+    an exact integer dot times both scales, rounded to fp32, the groups summed
+    in fp32 in ascending order.  Returns float32 [M, N]."""
+    qa = np.ascontiguousarray(qa, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.uint8)
+    qb = np.ascontiguousarray(qb, dtype=np.uint8)
+    sb = np.ascontiguousarray(sb, dtype=np.uint8)
+    M, N, K = qa.shape[0], qb.shape[0], qa.shape[1] * 2
+    C = np.empty((M, N), dtype=np.float32)
+    lib().oracle_gemm_f32(_p(qa), _p(sa), _p(qb), _p(sb), M, N, K, _p(C))
+    return C
+
+
+def num_threads() -> int:
+    """Threads the oracle's parallel loops use (OpenMP; OMP_NUM_THREADS)."""
+    return int(lib().oracle_num_threads())
+
+
 def gemm_f64_sampled(qa, sa, qb, sb, ms, ns) -> np.ndarray:
     qa = np.ascontiguousarray(qa, dtype=np.uint8)
     sa = np.ascontiguousarray(sa, dtype=np.uint8)
@@ -235,15 +253,16 @@ def bf16_from_f64(d: np.ndarray) -> np.ndarray:
     return out
 
 
-def mxfp4_gemm_bf16(a_bits: np.ndarray, qb: np.ndarray, sb: np.ndarray) -> np.ndarray:
-    """The whole per-call path: quantize bf16 A, multiply by quantized B, round to bf16 bits."""
+def mxfp4_gemm_bf16(a_bits: np.ndarray, qb: np.ndarray, sb: np.ndarray, f32acc: bool = False) -> np.ndarray:
+    """The whole per-call path: quantize bf16 A, multiply by quantized B (fp64,
+    or fp32 group accumulation), round to bf16 bits."""
     a = _u16(a_bits)
     qb = np.ascontiguousarray(qb, dtype=np.uint8)
     sb = np.ascontiguousarray(sb, dtype=np.uint8)
     M, K = a.shape
     N = qb.shape[0]
     C = np.empty((M, N), dtype=np.uint16)
-    rc = lib().oracle_mxfp4_gemm_bf16(_p(a), _p(qb), _p(sb), M, N, K, _p(C))
+    rc = lib().oracle_mxfp4_gemm_bf16(_p(a), _p(qb), _p(sb), M, N, K, _p(C), 1 if f32acc else 0)
     if rc != 0:
         raise ValueError("oracle_mxfp4_gemm_bf16: non-finite input")
     return C

@@ -7,7 +7,10 @@
  *
  * It is deliberately plain and slow: every quantity is computed from its
  * definition with exact integer arithmetic where the definition is integer,
- * and in fp64 where it is real-valued.
+ * and in fp64 where it is real-valued (the GEMM also in the fp32 group
+ * accumulation of the matrix unit).  Rows and output elements are
+ * independent and are computed in parallel (OpenMP); no result depends on
+ * the number of threads.
  *
  * Sources (three web pages, each a diff between two versions of a submission
  * to the "amd-mxfp4-mm" leaderboard; cited by submission number):
@@ -22,6 +25,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_API __attribute__((visibility("default")))
 
@@ -46,19 +52,6 @@ ORACLE_API double oracle_e8m0_value(int b)
 {
     if (b == 255) return NAN;
     return ldexp(1.0, b - 127);
-}
-
-/* bf16 bits -> exact double. */
-ORACLE_API double oracle_bf16_value(uint16_t h)
-{
-    int s = h >> 15;
-    int e = (h >> 7) & 0xFF;
-    int m = h & 0x7F;
-    double v;
-    if (e == 0xFF) v = m ? NAN : INFINITY;
-    else if (e == 0) v = ldexp((double)m, -133);
-    else v = ldexp((double)(128 + m), e - 134);
-    return s ? -v : v;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -137,38 +130,35 @@ ORACLE_API int oracle_encode(uint16_t x, int s)
 }
 
 /* ------------------------------------------------------------------------ */
-/* Element encoder, second formulation: the f32 bit manipulation of          */
-/* [711914, _mxfp4_quant_tile], written out in its order:                    */
-/*   qx = x * 2^-(s-127) in f32; strip the sign;                             */
-/*   qx >= 6          -> 7                                                   */
-/*   qx <  1          -> bits(qx + 2^22) - bits(2^22)   (f32 add rounds RNE) */
-/*   otherwise        -> (bits + ((1-127)<<23) + (1<<21) - 1 + bit22) >> 22  */
-/*   then OR the sign into bit 3.                                            */
-/* It must agree with oracle_encode on every input; the tests check that.    */
+/* Element encoder, second formulation: a nearest-value search.              */
+/* The same rule as oracle_encode, taken literally: v = |x| * 2^(127-s) in   */
+/* fp64 (exact: a bf16 value times a power of two within fp64's range),      */
+/* then the e2m1 magnitude at the least distance from v; when two are at the */
+/* same distance the even code wins; the sign goes to bit 3.  v is first     */
+/* capped at 8: every v >= 7 is nearest to 6 (code 7), and the cap keeps the */
+/* distances exact for huge v (where v - 4 and v - 6 would round to one      */
+/* double and fake a tie).  It shares nothing with oracle_encode but the     */
+/* magnitude table, and the tests require the two to agree on every input.   */
 /* ------------------------------------------------------------------------ */
-static uint32_t f2u(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
-static float u2f(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
-
-ORACLE_API int oracle_encode_bittrick(uint16_t x, int s)
+ORACLE_API int oracle_encode_nearest(uint16_t x, int s)
 {
-    float xf = u2f((uint32_t)x << 16);
-    volatile float scale_inv = (float)ldexp(1.0, 127 - s); /* exact in f32 for s in [0,254] */
-    float qx = xf * scale_inv;
-    uint32_t qu = f2u(qx);
-    uint32_t sign = qu & 0x80000000u;
-    qu ^= sign;
-    float qf = u2f(qu);
-    uint32_t code;
-    if (qf >= 6.0f) {
-        code = 7;
-    } else if (qf < 1.0f) {
-        volatile float t = qf + 4194304.0f;
-        code = (f2u(t) - 0x4A800000u) & 0xFF;
-    } else {
-        uint32_t odd = (qu >> 22) & 1;
-        code = ((qu + 0xC11FFFFFu + odd) >> 22) & 0xFF;
+    static const double mags[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    int sign = (x >> 15) & 1;
+    int e = (x >> 7) & 0xFF;
+    int m = x & 0x7F;
+    double ax = (e == 0) ? ldexp((double)m, -133) : ldexp((double)(128 + m), e - 134);
+    double v = ldexp(ax, 127 - s);
+    if (v > 8.0) v = 8.0;
+    int best = 0;
+    double best_d = fabs(v - mags[0]);
+    for (int c = 1; c < 8; c++) {
+        double d = fabs(v - mags[c]);
+        if (d < best_d || (d == best_d && c % 2 == 0)) {
+            best = c;
+            best_d = d;
+        }
     }
-    return (int)(code | (sign >> 28));
+    return (sign << 3) | best;
 }
 
 /* Vector forms for exhaustive sweeps. */
@@ -177,9 +167,9 @@ ORACLE_API void oracle_encode_many(const uint16_t *x, const uint8_t *s, int64_t 
     for (int64_t i = 0; i < n; i++) out[i] = (uint8_t)oracle_encode(x[i], s[i]);
 }
 
-ORACLE_API void oracle_encode_bittrick_many(const uint16_t *x, const uint8_t *s, int64_t n, uint8_t *out)
+ORACLE_API void oracle_encode_nearest_many(const uint16_t *x, const uint8_t *s, int64_t n, uint8_t *out)
 {
-    for (int64_t i = 0; i < n; i++) out[i] = (uint8_t)oracle_encode_bittrick(x[i], s[i]);
+    for (int64_t i = 0; i < n; i++) out[i] = (uint8_t)oracle_encode_nearest(x[i], s[i]);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -193,12 +183,14 @@ ORACLE_API void oracle_encode_bittrick_many(const uint16_t *x, const uint8_t *s,
 ORACLE_API int oracle_quantize(const uint16_t *x, int64_t rows, int64_t K, uint8_t *q, uint8_t *scales)
 {
     if (K % 32 != 0) return -1;
+    for (int64_t i = 0; i < rows * K; i++)
+        if (((x[i] >> 7) & 0xFF) == 0xFF) return -1;
     int64_t G = K / 32;
+    /* rows are independent */
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; r++) {
         for (int64_t g = 0; g < G; g++) {
             const uint16_t *grp = x + r * K + g * 32;
-            for (int j = 0; j < 32; j++)
-                if (((grp[j] >> 7) & 0xFF) == 0xFF) return -1;
             int s = oracle_scale_byte(grp, 32);
             scales[r * G + g] = (uint8_t)s;
             for (int j = 0; j < 32; j += 2) {
@@ -215,6 +207,7 @@ ORACLE_API int oracle_quantize(const uint16_t *x, int64_t rows, int64_t K, uint8
 ORACLE_API void oracle_dequantize(const uint8_t *q, const uint8_t *scales, int64_t rows, int64_t K, double *out)
 {
     int64_t G = K / 32;
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; r++)
         for (int64_t k = 0; k < K; k++) {
             uint8_t byte = q[r * (K / 2) + k / 2];
@@ -303,9 +296,27 @@ ORACLE_API void oracle_unpreshuffle_b(const uint8_t *sh, int64_t N, int64_t K, u
 /*   C[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k]                             */
 /* where deq() is value(code) * 2^(scale-127) per 32-group.                  */
 /* [608632, kernel v7: the scaled dot of two e2m1 operands with e8m0 scales  */
-/* into an accumulator].  Computed in fp64 (each product is exact; the sum   */
-/* rounds at ~1e-16 relative).  Returns the fp64 values.                     */
+/* into an accumulator].  Two accumulations are provided:                    */
+/*   oracle_gemm_f64  fp64, k ascending.  Each product is exact and the sum  */
+/*                    rounds at ~1e-16 relative: the exact product for all   */
+/*                    practical purposes (exact on small shapes).            */
+/*   oracle_gemm_f32  the matrix unit's own precision: per 32-group the      */
+/*                    integer dot of the codes (exact), times both scales,   */
+/*                    converted to fp32, then the groups summed in fp32 in   */
+/*                    ascending group order [608632, kernel v7: an f32       */
+/*                    accumulator over the K loop].                          */
+/* Output elements are independent, so they are computed in parallel        */
+/* (OpenMP over (m, n)); each one's arithmetic is the plain loop below.      */
 /* ------------------------------------------------------------------------ */
+ORACLE_API int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 ORACLE_API void oracle_gemm_f64(const uint8_t *qa, const uint8_t *sa, const uint8_t *qb, const uint8_t *sb,
                                 int64_t M, int64_t N, int64_t K, double *C)
 {
@@ -313,6 +324,7 @@ ORACLE_API void oracle_gemm_f64(const uint8_t *qa, const uint8_t *sa, const uint
     double *db = (double *)malloc(sizeof(double) * (size_t)(N * K));
     oracle_dequantize(qa, sa, M, K, da);
     oracle_dequantize(qb, sb, N, K, db);
+#pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; m++)
         for (int64_t n = 0; n < N; n++) {
             double acc = 0.0;
@@ -323,7 +335,41 @@ ORACLE_API void oracle_gemm_f64(const uint8_t *qa, const uint8_t *sa, const uint
     free(db);
 }
 
-/* Same sum for selected output elements only (for full-size parity
+/* Twice the e2m1 value of a code: an integer in {0, 1, 2, 3, 4, 6, 8, 12},  */
+/* signed (the table of oracle_e2m1_value, doubled).                         */
+static int e2m1_twice(int code)
+{
+    static const int mag2[8] = {0, 1, 2, 3, 4, 6, 8, 12};
+    return (code & 8) ? -mag2[code & 7] : mag2[code & 7];
+}
+
+ORACLE_API void oracle_gemm_f32(const uint8_t *qa, const uint8_t *sa, const uint8_t *qb, const uint8_t *sb,
+                                int64_t M, int64_t N, int64_t K, float *C)
+{
+    int64_t G = K / 32;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++) {
+            float acc = 0.0f;
+            for (int64_t g = 0; g < G; g++) {
+                /* integer dot in units of 1/4: sum of (2 a)(2 b) over the group */
+                int64_t dot4 = 0;
+                for (int64_t j = 0; j < 32; j++) {
+                    int64_t k = 32 * g + j;
+                    uint8_t ba = qa[m * (K / 2) + k / 2], bb = qb[n * (K / 2) + k / 2];
+                    int ca = (k % 2 == 0) ? (ba & 0xF) : (ba >> 4);
+                    int cb = (k % 2 == 0) ? (bb & 0xF) : (bb >> 4);
+                    dot4 += (int64_t)e2m1_twice(ca) * e2m1_twice(cb);
+                }
+                /* exact in fp64 (|dot4| <= 4608); one rounding to fp32 */
+                double term = ldexp((double)dot4, (int)sa[m * G + g] + (int)sb[n * G + g] - 254 - 2);
+                acc = acc + (float)term;
+            }
+            C[m * N + n] = acc;
+        }
+}
+
+/* Same fp64 sum for selected output elements only (for full-size parity
  * sampling): C_out[i] = C[ms[i]][ns[i]]. */
 ORACLE_API void oracle_gemm_f64_sampled(const uint8_t *qa, const uint8_t *sa, const uint8_t *qb, const uint8_t *sb,
                                         int64_t M, int64_t N, int64_t K, const int64_t *ms, const int64_t *ns,
@@ -332,6 +378,7 @@ ORACLE_API void oracle_gemm_f64_sampled(const uint8_t *qa, const uint8_t *sa, co
     (void)M;
     (void)N;
     int64_t G = K / 32;
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < count; i++) {
         int64_t m = ms[i], n = ns[i];
         double acc = 0.0;
@@ -349,8 +396,12 @@ ORACLE_API void oracle_gemm_f64_sampled(const uint8_t *qa, const uint8_t *sa, co
 /* ------------------------------------------------------------------------ */
 /* fp64 -> bf16 bits, round to nearest, ties to even, directly from the      */
 /* double (no intermediate f32 rounding).  Reading: the pages cast the f32   */
-/* accumulator to bf16 without naming a mode; nearest-even is taken.         */
+/* accumulator to bf16 without naming a mode; nearest-even is taken.  An     */
+/* fp32 accumulator converts to fp64 exactly, so this also rounds the fp32   */
+/* mode's results.                                                           */
 /* ------------------------------------------------------------------------ */
+static uint32_t f2u(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
 ORACLE_API uint16_t oracle_bf16_from_f64(double d)
 {
     if (isnan(d)) return 0x7FC0;
@@ -375,21 +426,29 @@ ORACLE_API void oracle_bf16_from_f64_many(const double *d, int64_t n, uint16_t *
 
 /* ------------------------------------------------------------------------ */
 /* The whole per-call path from bf16 A: quantize A, GEMM against quantized   */
-/* B given in natural layout, round to bf16.  Used for the CPU baseline.     */
+/* B given in natural layout (fp32 group accumulation when f32acc != 0, else */
+/* fp64), round to bf16.  Used for the CPU baseline.                         */
 /* ------------------------------------------------------------------------ */
 ORACLE_API int oracle_mxfp4_gemm_bf16(const uint16_t *A, const uint8_t *qb, const uint8_t *sb, int64_t M, int64_t N,
-                                      int64_t K, uint16_t *C)
+                                      int64_t K, uint16_t *C, int f32acc)
 {
     uint8_t *qa = (uint8_t *)malloc((size_t)(M * K / 2));
     uint8_t *sa = (uint8_t *)malloc((size_t)(M * K / 32));
     double *c64 = (double *)malloc(sizeof(double) * (size_t)(M * N));
+    float *c32 = f32acc ? (float *)malloc(sizeof(float) * (size_t)(M * N)) : NULL;
     int rc = oracle_quantize(A, M, K, qa, sa);
     if (rc == 0) {
-        oracle_gemm_f64(qa, sa, qb, sb, M, N, K, c64);
+        if (f32acc) {
+            oracle_gemm_f32(qa, sa, qb, sb, M, N, K, c32);
+            for (int64_t i = 0; i < M * N; i++) c64[i] = (double)c32[i];
+        } else {
+            oracle_gemm_f64(qa, sa, qb, sb, M, N, K, c64);
+        }
         oracle_bf16_from_f64_many(c64, M * N, C);
     }
     free(qa);
     free(sa);
     free(c64);
+    free(c32);
     return rc;
 }

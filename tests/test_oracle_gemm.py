@@ -162,3 +162,135 @@ def test_bf16_rounding_matches_integer_rne_on_f32_values():
     want = f32_to_bf16_bits(x)
     got = oracle.bf16_from_f64(x.astype(np.float64))
     assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- fp32 accumulation
+
+def group_terms(qa, sa, qb, sb):
+    """Exact per-group terms t[m, n, g] = sum over the group of deq(A) deq(B)
+    (numpy fp64 on dequantized values: every product and every 32-term sum
+    of e2m1 x e2m1 x powers of two within one group is exact)."""
+    M, N, K = qa.shape[0], qb.shape[0], qa.shape[1] * 2
+    da = oracle.dequantize(qa, sa).reshape(M, K // 32, 32)
+    db = oracle.dequantize(qb, sb).reshape(N, K // 32, 32)
+    return np.einsum("mgj,ngj->mng", da, db)
+
+
+def f32_ascending(terms):
+    """Reference fp32 accumulation, one element at a time: round each group
+    term to fp32 and add in ascending group order with numpy float32 adds."""
+    acc = np.float32(0.0)
+    for t in terms:
+        acc = np.float32(acc + np.float32(t))
+    return acc
+
+
+@pytest.mark.parametrize("M,N,K,seed", [(2, 3, 256, 1), (3, 5, 512, 2), (1, 4, 1024, 3)])
+def test_gemm_f32_matches_elementwise_fp32_emulation(M, N, K, seed):
+    a = normal_bf16(seed, 0, (M, K))
+    b = normal_bf16(seed, 1, (N, K))
+    a[0, :32] = f32_to_bf16_bits(np.float32(1e4) * bf16_bits_to_f32(a[0, :32]))  # one large group
+    qa, sa = oracle.quantize(a)
+    qb, sb = oracle.quantize(b)
+    C = oracle.gemm_f32(qa, sa, qb, sb)
+    t = group_terms(qa, sa, qb, sb)
+    for m in range(M):
+        for n in range(N):
+            assert C[m, n] == f32_ascending(t[m, n]), (m, n)
+
+
+def test_gemm_f32_equals_f64_where_the_sums_are_exact():
+    """All scale bytes 127 and K = 512: every partial sum is a multiple of
+    1/4 below 2^12, exact in fp32, so the two accumulations agree exactly."""
+    rng = np.random.default_rng(11)
+    M, N, K = 9, 40, 512
+    qa = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    qb = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    sa = np.full((M, K // 32), 127, dtype=np.uint8)
+    sb = np.full((N, K // 32), 127, dtype=np.uint8)
+    c32 = oracle.gemm_f32(qa, sa, qb, sb)
+    c64 = oracle.gemm_f64(qa, sa, qb, sb)
+    assert np.array_equal(c32.astype(np.float64), c64)
+
+
+def test_gemm_f32_adds_groups_in_ascending_order():
+    """Three groups, each with a single nonzero product, so the group terms
+    are exactly +-2^25 and 1.  Row 0 has terms (2^25, 1, -2^25): in fp32 and
+    ascending order (2^25 + 1) rounds to 2^25 (the fp32 spacing there is 4),
+    and the sum is 0.  Row 1 has (2^25, -2^25, 1) and sums to 1.  fp64 gives
+    1 for both, and adding row 0's groups in any order that pairs 2^25 with
+    -2^25 first gives 1: only ascending fp32 accumulation gives (0, 1)."""
+    K = 96
+    qa = np.zeros((2, K // 2), dtype=np.uint8)
+    qb = np.zeros((1, K // 2), dtype=np.uint8)
+    sa = np.full((2, 3), 127, dtype=np.uint8)
+    sb = np.full((1, 3), 127, dtype=np.uint8)
+    # codes: 2 = 1.0, 0xA = -1.0; element 0 of each group
+    qb[0, 0] = qb[0, 16] = qb[0, 32] = 0x02
+    # row 0: +2^25, +1, -2^25 ; row 1: +2^25, -2^25, +1
+    qa[0, 0], qa[0, 16], qa[0, 32] = 0x02, 0x02, 0x0A
+    qa[1, 0], qa[1, 16], qa[1, 32] = 0x02, 0x0A, 0x02
+    sa[0] = [127 + 25, 127, 127 + 25]
+    sa[1] = [127 + 25, 127 + 25, 127]
+    C = oracle.gemm_f32(qa, sa, qb, sb)
+    assert C[0, 0] == 0.0   # 2^25 + 1 rounds to 2^25, then cancels
+    assert C[1, 0] == 1.0   # 2^25 - 2^25 = 0, then + 1
+    assert list(oracle.gemm_f64(qa, sa, qb, sb)[:, 0]) == [1.0, 1.0]
+
+
+@pytest.mark.parametrize("M,N,K,seed", [(16, 96, 1536, 1), (8, 64, 7168, 3), (32, 64, 2048, 4)])
+def test_gemm_f32_gap_to_f64_within_summation_bound(M, N, K, seed):
+    """|C32 - C64| <= gamma_G * sum_g |t_g| with gamma_G = G u / (1 - G u),
+    u = 2^-24: the error bound of recursive summation of G terms, each
+    term itself rounded once to fp32 (Higham, Accuracy and Stability of
+    Numerical Algorithms, 2nd ed., section 4.2).  Far below the method's
+    tolerance of 1e-2 |C| + 1e-2."""
+    a = normal_bf16(seed, 0, (M, K))
+    b = normal_bf16(seed, 1, (N, K))
+    qa, sa = oracle.quantize(a)
+    qb, sb = oracle.quantize(b)
+    c32 = oracle.gemm_f32(qa, sa, qb, sb).astype(np.float64)
+    c64 = oracle.gemm_f64(qa, sa, qb, sb)
+    t = group_terms(qa, sa, qb, sb)
+    G = K // 32
+    u = 2.0 ** -24
+    gamma = (G + 1) * u / (1 - (G + 1) * u)
+    bound = gamma * np.abs(t).sum(axis=2)
+    assert np.all(np.abs(c32 - c64) <= bound)
+    assert np.all(np.abs(c32 - c64) <= 1e-3 * (1e-2 * np.abs(c64) + 1e-2))
+
+
+def test_whole_path_with_f32_accumulation():
+    a = normal_bf16(8, 0, (5, 256))
+    b = normal_bf16(8, 1, (32, 256))
+    qa, sa = oracle.quantize(a)
+    qb, sb = oracle.quantize(b)
+    want = oracle.bf16_from_f64(oracle.gemm_f32(qa, sa, qb, sb).astype(np.float64))
+    assert np.array_equal(oracle.mxfp4_gemm_bf16(a, qb, sb, f32acc=True), want)
+
+
+def test_results_do_not_depend_on_thread_count(tmp_path):
+    """The parallel loops split independent outputs only: one thread and
+    many give the same bytes (run in a child process with OMP_NUM_THREADS=1)."""
+    import os
+    import subprocess
+    import sys
+    out = str(tmp_path / "one.npy")
+    code = ("import sys, numpy as np, oracle, synthetic as s\n"
+            "a = s.normal_bf16(21, 0, (12, 1024)); b = s.normal_bf16(21, 1, (80, 1024))\n"
+            "qa, sa = oracle.quantize(a); qb, sb = oracle.quantize(b)\n"
+            "assert oracle.num_threads() == 1\n"
+            "np.save(sys.argv[1], np.concatenate([oracle.gemm_f64(qa, sa, qb, sb).ravel(), "
+            "oracle.gemm_f32(qa, sa, qb, sb).astype(np.float64).ravel()]))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, OMP_NUM_THREADS="1", PYTHONPATH=root)
+    subprocess.run([sys.executable, "-c", code, out], env=env, check=True, cwd=root)
+    one = np.load(out)
+    a = normal_bf16(21, 0, (12, 1024))
+    b = normal_bf16(21, 1, (80, 1024))
+    qa, sa = oracle.quantize(a)
+    qb, sb = oracle.quantize(b)
+    many = np.concatenate([oracle.gemm_f64(qa, sa, qb, sb).ravel(),
+                           oracle.gemm_f32(qa, sa, qb, sb).astype(np.float64).ravel()])
+    assert oracle.num_threads() > 1 or os.cpu_count() == 1
+    assert np.array_equal(one, many)

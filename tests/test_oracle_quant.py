@@ -71,12 +71,13 @@ def nearest_even_search(x_bits, s):
 
 
 def test_encoder_exhaustive_three_formulations():
-    """All finite bf16 x all scale bytes 0..254: integer encoder == f32 bit
-    trick of the pages == nearest-even search."""
+    """All finite bf16 x all scale bytes 0..254: the integer midpoint
+    encoder == the oracle's fp64 distance search == this file's numpy
+    nearest-even search."""
     x = finite_bf16_all()
     for s in range(255):
         a = oracle.encode_many(x, s)
-        b = oracle.encode_bittrick_many(x, s)
+        b = oracle.encode_nearest_many(x, s)
         c = nearest_even_search(x, s)
         assert np.array_equal(a, b), s
         assert np.array_equal(a, c), (s, np.nonzero(a != c)[0][:5])
