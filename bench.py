@@ -1,28 +1,38 @@
 #!/usr/bin/env python3
-"""Benchmark of the fused MXFP4 GEMM (A bf16 quantized on the fly) on one MI355X.
+"""Benchmark of the MXFP4 GEMM (A bf16 quantized on the fly) on one MI355X.
 
-A step is one call of the whole per-call path -- quantize A in registers,
-multiply by the preshuffled MXFP4 B, reduce, store bf16 C -- over one batch of
-synthetic input.  B is prepared once, outside the timed region, by the
-library's own quantize and preshuffle kernels.
+A step is one call of the whole per-call path -- quantize A, multiply by the
+preshuffled MXFP4 B with scaled FP4 matrix instructions, reduce, store bf16 C
+-- over one batch of synthetic input.  B is prepared once, outside the timed
+region, by the library's own quantize and preshuffle kernels.
 
-Timing: K steps are captured into one HIP graph and replayed; the timed
-region is that replay, bracketed by device synchronizations, with HIP events
-recorded on the replay stream.  In the default "cold" mode consecutive steps
-cycle through enough copies of (A, B, scales, C) -- at least 1 GiB -- that
-each step's inputs come from HBM rather than L2 or the 256 MB MALL.
+Cold by construction, at any step count: every configuration gets S copies
+("sets") of (A, B, scales, C), S a multiple of --steps with S * set bytes >=
+1 GiB (4x the 256 MB MALL).  The calls cycle through the sets in order, so a
+set is touched again only after every other set has been: each call's inputs
+were last read >= 1 GiB of other traffic ago and come from HBM.  The calls
+are captured as S / steps HIP graphs of --steps calls each, replayed in turn
+so the rotation continues from one replay to the next.
 
-Each configuration is then timed a second time on a single buffer set
-("warm_us_per_call": inputs stay in L2 and the MALL), for context; the
-reported value is always the cold one.
+Timed region: one replay of the next graph (exactly --steps calls, each on
+its own set), bracketed by device synchronizations, with HIP events recorded
+on the replay stream; ms_per_step is that replay's event time / steps.
+Statistics: further replays (the rotation continuing), each timed by events,
+give the median, p10 and p90 of the time per call.
 
-Prints one JSON line.  The headline workload is M=32, N=4096, K=512; the
-line also carries every measured configuration under "per_config".
+The headline is the largest configuration, M=256 N=7168 K=7168, reported as
+TFLOP/s against the dense MXFP4 matrix peak.  Every configuration (the five
+of the method's workloads and the other leaderboard shapes on the pages) is
+reported under per_config with its own roofline block; for context each is
+also timed warm (one set, inputs resident in L2 and the MALL).
+
+Prints one JSON line.
 """
 import argparse
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -32,13 +42,72 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 matrix peak, TFLOP/s
-HEADLINE = "c2"
-# What decides the headline GEMM's code: its kernel sources, plus the
-# schedule the library picks for the headline shape (hashed with them).
-KERNEL_SOURCES = ["block_scaled_mxfp4_bf16_amd/csrc/gemm_kernels.hip", "block_scaled_mxfp4_bf16_amd/csrc/mxfp4_device.hpp",
-                  "block_scaled_mxfp4_bf16_amd/csrc/mxfp4_internal.hpp"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_M32_N4096_K512.json")
+HEADLINE = "c5"
+COLD_BYTES = 1 << 30           # footprint of one rotation: 4x the 256 MB MALL
+# What decides the kernels' code: the library sources, plus the schedule the
+# library picks for the headline shape (hashed with them).
+KERNEL_SOURCE_DIR = "block_scaled_mxfp4_bf16_amd/csrc"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_M256_N7168_K7168.json")
 CALIBRATION_BYTES = 256 << 20
+
+
+def alg_bytes(M, N, K):
+    """A bf16 + B e2m1 + B e8m0 + C bf16, each counted once."""
+    return 2 * M * K + N * K // 2 + N * K // 32 + 2 * M * N
+
+
+def alg_flops(M, N, K):
+    return 2 * M * N * K
+
+
+def expected_mfma(M, N, K):
+    """Matrix instructions the product needs at 16 x 16 x 128 per
+    instruction: 16-row tiles (rows past M padded), 16-column subtiles,
+    128-wide K steps (a final 64-wide half step counted whole)."""
+    return ((M + 15) // 16) * (N // 16) * ((K + 127) // 128)
+
+
+def set_bytes(M, N, K):
+    """Device bytes of one buffer set: A, B codes, padded B scales, C."""
+    scales = ((N + 255) // 256 * 256) * ((K // 32 + 7) // 8 * 8)
+    return 2 * M * K + N * K // 2 + scales + 2 * M * N
+
+
+def rotation(per_set, steps, min_bytes=COLD_BYTES):
+    """(sets, graphs): the least multiple of `steps` sets whose footprint is
+    at least min_bytes, and the number of `steps`-call graphs that cover them."""
+    need = max(1, math.ceil(min_bytes / per_set))
+    sets = steps * math.ceil(need / steps)
+    return sets, sets // steps
+
+
+def percentile(v, q):
+    """Linear-interpolated percentile of a list (q in [0, 100])."""
+    s = sorted(v)
+    if len(s) == 1:
+        return s[0]
+    x = (len(s) - 1) * q / 100.0
+    i = int(math.floor(x))
+    j = min(i + 1, len(s) - 1)
+    return s[i] + (s[j] - s[i]) * (x - i)
+
+
+def roofline(M, N, K, us, bound):
+    """Roofline block for one configuration at `us` microseconds per call:
+    algorithmic bytes against HBM, or algorithmic FLOPs against the MXFP4
+    matrix peak."""
+    if bound == "mfma":
+        achieved = alg_flops(M, N, K) / (us * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP4_PEAK_TFLOPS, 4)}
+    achieved = alg_bytes(M, N, K) / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4)}
+
+
+def bound_of(M):
+    """The method's targets: HBM roofline at small M, matrix peak from 256 rows."""
+    return "mfma" if M >= 256 else "hbm"
 
 
 def calibration_copy(torch):
@@ -62,8 +131,10 @@ def kernel_source_hash():
     import block_scaled_mxfp4_bf16_amd as mx
     import synthetic as syn
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
+    d = os.path.join(ROOT, KERNEL_SOURCE_DIR)
+    for rel in sorted(os.listdir(d)):
+        with open(os.path.join(d, rel), "rb") as f:
+            h.update(rel.encode())
             h.update(f.read())
     w = syn.CONFIGS[HEADLINE]
     h.update(str(mx.mxfp4_gemm_schedule_name(w.M, w.N, w.K)).encode())
@@ -71,8 +142,8 @@ def kernel_source_hash():
 
 
 def measured_traffic():
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the kernel as it is now; else None."""
+    """HBM bytes per call of the headline workload from the committed counter
+    summary, if it was taken on the kernels as they are now; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -80,16 +151,29 @@ def measured_traffic():
         return None
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get("hbm_bytes_per_call")
 
 
-def alg_bytes(M, N, K):
-    """A bf16 + B e2m1 + B e8m0 + C bf16, each counted once."""
-    return 2 * M * K + N * K // 2 + N * K // 32 + 2 * M * N
+def gpu_clocks():
+    """Current GPU clocks as amd-smi reports them (JSON), or the error."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        if r.returncode != 0:
+            return {"error": (r.stderr or r.stdout).strip()[-300:]}
+        return json.loads(r.stdout)
+    except Exception as e:  # the clocks are context; the measurement does not depend on them
+        return {"error": repr(e)[-300:]}
 
 
-def alg_flops(M, N, K):
-    return 2 * M * N * K
+def cpu_model():
+    try:
+        for line in subprocess.run(["lscpu"], capture_output=True, text=True, timeout=30).stdout.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return None
 
 
 def prepare(torch, mx, w, sets):
@@ -110,10 +194,13 @@ def prepare(torch, mx, w, sets):
     return out
 
 
-def time_config(torch, mx, w, steps, warmup, cold):
+def time_config(torch, mx, w, steps, warmup, samples, cold=True):
+    """Time `steps`-call graph replays of the workload (see the module
+    docstring).  Returns the per-call figures of the first timed replay (the
+    contract's timed region) and the statistics over `samples` replays."""
     M, N, K = w.M, w.N, w.K
-    per_set = alg_bytes(M, N, K) + N * K // 32
-    sets = min(512, max(2, math.ceil((1 << 30) / per_set))) if cold else 1
+    per_set = set_bytes(M, N, K)
+    sets, graphs = rotation(per_set, steps) if cold else (1, 1)
     bufs = prepare(torch, mx, w, sets)
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
@@ -122,40 +209,61 @@ def time_config(torch, mx, w, steps, warmup, cold):
             A, Bw, Bs, C = bufs[i % sets]
             mx.mxfp4_gemm(A, Bw, Bs, C, M, N, K, stream=stream)
     stream.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for i in range(steps):
-            A, Bw, Bs, C = bufs[i % sets]
-            mx.mxfp4_gemm(A, Bw, Bs, C, M, N, K, stream=stream)
+    gs = []
+    for j in range(graphs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                A, Bw, Bs, C = bufs[(j * steps + i) % sets]
+                mx.mxfp4_gemm(A, Bw, Bs, C, M, N, K, stream=stream)
+        gs.append(g)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
-        g.replay()  # first replay uploads the graph
+        for g in gs:
+            g.replay()  # the first replay of a graph uploads it
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
+    # the timed region: one replay, exactly `steps` calls
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
-        ev0.record(stream)
-        g.replay()
-        ev1.record(stream)
+        ev[0][0].record(stream)
+        gs[0].replay()
+        ev[0][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = ev0.elapsed_time(ev1) / steps
-    del g, bufs
+    # statistics: the rotation continues through the graphs in order
+    with torch.cuda.stream(stream):
+        for s in range(1, samples):
+            ev[s][0].record(stream)
+            gs[s % graphs].replay()
+            ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    us = [a.elapsed_time(b) * 1e3 / steps for a, b in ev]
+    del gs, bufs
     torch.cuda.empty_cache()
-    us = kern_ms * 1e3
-    return {
+    med = percentile(us, 50)
+    r = {
         "M": M, "N": N, "K": K,
         "schedule": mx.mxfp4_gemm_schedule_name(M, N, K),
-        "buffer_sets": sets,
-        "us_per_call": round(us, 4),
-        "wall_ms_per_step": wall * 1e3 / steps,
-        "tflops": alg_flops(M, N, K) / (us * 1e-6) / 1e12,
-        "alg_gbs": alg_bytes(M, N, K) / (us * 1e-6) / 1e9,
-        "hbm_frac": alg_bytes(M, N, K) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-        "mfma_frac": alg_flops(M, N, K) / (us * 1e-6) / 1e12 / FP4_PEAK_TFLOPS,
+        "cache": ("cold: %d buffer sets of %d bytes (%.2f GiB) cycled in order; each call's set last touched %d "
+                  "calls earlier" % (sets, per_set, sets * per_set / 2 ** 30, sets)) if cold else
+                 "warm: one buffer set (inputs resident in L2 and MALL)",
+        "buffer_sets": sets, "set_bytes": per_set, "footprint_bytes": sets * per_set,
+        "timed_us_per_call": round(us[0], 4),
+        "timed_wall_ms": round(wall * 1e3, 4),
+        "samples": samples, "calls_per_sample": steps,
+        "us_per_call": round(med, 4),
+        "us_p10": round(percentile(us, 10), 4), "us_p90": round(percentile(us, 90), 4),
+        "us_min": round(min(us), 4), "us_max": round(max(us), 4),
+        "tflops": alg_flops(M, N, K) / (med * 1e-6) / 1e12,
+        "alg_gbs": alg_bytes(M, N, K) / (med * 1e-6) / 1e9,
+        "hbm_frac": alg_bytes(M, N, K) / (med * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "mfma_frac": alg_flops(M, N, K) / (med * 1e-6) / 1e12 / FP4_PEAK_TFLOPS,
     }
+    r["roofline"] = roofline(M, N, K, med, bound_of(M))
+    return r
 
 
 def time_prepare_b(torch, mx, w, steps=50):
@@ -164,7 +272,7 @@ def time_prepare_b(torch, mx, w, steps=50):
     import numpy as np
     N, K = w.N, w.K
     b = torch.from_numpy(w.b_bits().view(np.int16)).view(torch.bfloat16).to("cuda")
-    sets = max(2, math.ceil((1 << 30) / (2 * N * K)))
+    sets = max(2, math.ceil(COLD_BYTES / (2 * N * K)))
     bs_in = [b] + [b.clone() for _ in range(sets - 1)]
     bw = torch.empty((N // 16, (K // 2) * 16), dtype=torch.uint8, device="cuda")
     bs = torch.empty(mx.mxfp4_shuffled_scale_bytes(N, K), dtype=torch.uint8, device="cuda")
@@ -195,24 +303,52 @@ def time_prepare_b(torch, mx, w, steps=50):
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "buffer_sets": sets}
 
 
-def cpu_baseline(w, budget_s=12.0):
-    """The oracle as it stands, single-threaded, on whole calls of the
-    headline workload (quantize A, exact GEMM, round) until the budget is
-    spent."""
+CPU_SAMPLE_ROWS = 8  # rows of the headline workload's A in the oracle's sample
+
+
+def _cpu_leg(rows, budget_s):
+    """Whole calls of the oracle (quantize A, fp32 group-accumulated GEMM,
+    bf16 rounding) on the first `rows` rows of the headline workload, until
+    the budget is spent: (TFLOP/s, calls, seconds, threads)."""
     import oracle
+    import synthetic as syn
+    w = syn.CONFIGS[HEADLINE]
     qb, sb = oracle.quantize(w.b_bits())
-    a = w.a_bits()
-    oracle.mxfp4_gemm_bf16(a, qb, sb)  # load + page in
+    a = w.a_bits()[:rows].copy()
+    oracle.mxfp4_gemm_bf16(a, qb, sb, f32acc=True)  # load + page in
     n = 0
     t0 = time.perf_counter()
     while True:
-        oracle.mxfp4_gemm_bf16(a, qb, sb)
+        oracle.mxfp4_gemm_bf16(a, qb, sb, f32acc=True)
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    return {"value": alg_flops(w.M, w.N, w.K) * n / el / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": "%d whole calls of %s (quantize A + fp64 GEMM + bf16 rounding), %.1f s" % (n, w.name, el)}
+    return alg_flops(rows, w.N, w.K) * n / el / 1e12, n, el, oracle.num_threads()
+
+
+def cpu_baseline(threads, budget_s=10.0):
+    """The oracle as it stands, on the host's cores: all `threads` threads,
+    then one thread (each leg in a child process, so its OpenMP thread count
+    is fixed at start; neither touches the GPU)."""
+    import synthetic as syn
+    w = syn.CONFIGS[HEADLINE]
+    legs = {}
+    for nt in (threads, 1):
+        code = ("import json, sys; sys.path.insert(0, %r); import bench; "
+                "print(json.dumps(bench._cpu_leg(%d, %r)))" % (ROOT, CPU_SAMPLE_ROWS, budget_s))
+        env = dict(os.environ, OMP_NUM_THREADS=str(nt), HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="")
+        out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=600,
+                             check=True).stdout
+        legs[nt] = json.loads(out.strip().splitlines()[-1])
+    v, n, el, used = legs[threads]
+    v1, n1, el1, _ = legs[1]
+    sample = ("%d whole calls (quantize A + fp32 group-accumulated GEMM + bf16 rounding) on rows 0-%d of %s "
+              "(%d x %d x %d), %.1f s" % (n, CPU_SAMPLE_ROWS - 1, w.name, CPU_SAMPLE_ROWS, w.N, w.K, el))
+    return {"value": v, "unit": "TFLOP/s", "cores": used, "kind": "oracle", "sample": sample,
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "single_thread": {"value": v1, "unit": "TFLOP/s", "cores": 1,
+                              "sample": "%d whole calls, %.1f s" % (n1, el1)}}
 
 
 def _pmc_rows(d):
@@ -227,50 +363,46 @@ def _pmc_rows(d):
 
 def summarize_pmc(fetch_dir, write_dir, command):
     """Turn two rocprofv3 --pmc runs of the headline bench (FETCH_SIZE, then
-    WRITE_SIZE; KiB per dispatch) into HBM bytes per GEMM launch.  The scale
-    of each counter is calibrated on the plain copy kernels of the same runs
-    (the clones of B, of known size, made while preparing the buffer sets)."""
+    WRITE_SIZE; KiB per dispatch) into HBM bytes per call: per kernel of the
+    call (the library's kernels), the median over its dispatches, summed.
+    Each counter is scaled by what it reads for a plain copy of known size
+    (the largest copy of the run: the 256 MiB calibration copy)."""
     import synthetic as syn
     w = syn.CONFIGS[HEADLINE]
-    bw_bytes = w.N * w.K // 2
+    med = lambda v: sorted(v)[len(v) // 2]
 
     def per_kernel(rows, counter):
-        gemm, copy = [], []
+        kern, copy = {}, []
         for r in rows:
             if r["Counter_Name"] != counter:
                 continue
             v = float(r["Counter_Value"]) * 1024.0
             name = r["Kernel_Name"]
-            if "gemm_kernel" in name:
-                gemm.append(v)
+            if "mxfp4::" in name:
+                kern.setdefault(name.split("(")[0], []).append(v)
             elif "copyBuffer" in name:
                 copy.append((int(r["Grid_Size"]), v))
-        # the calibration copy is the largest copy of the run
         big = max(g for g, _ in copy)
-        return gemm, [v for g, v in copy if g == big]
+        return kern, [v for g, v in copy if g == big]
 
-    fg, fc = per_kernel(_pmc_rows(fetch_dir), "FETCH_SIZE")
-    wg, wc = per_kernel(_pmc_rows(write_dir), "WRITE_SIZE")
-    med = lambda v: sorted(v)[len(v) // 2]
+    fk, fc = per_kernel(_pmc_rows(fetch_dir), "FETCH_SIZE")
+    wk, wc = per_kernel(_pmc_rows(write_dir), "WRITE_SIZE")
     f_scale = med(fc) / CALIBRATION_BYTES  # counter bytes per byte copied
     w_scale = med(wc) / CALIBRATION_BYTES
-    fetch = med(fg) / f_scale
-    write = med(wg) / w_scale
-    out = {"workload": w.name, "kernel_source_hash": kernel_source_hash(), "command": command,
-           "gemm_dispatches": [len(fg), len(wg)], "fetch_bytes_per_launch": round(fetch),
-           "write_bytes_per_launch": round(write), "hbm_bytes_per_launch": round(fetch + write),
+    kernels = {}
+    for name in sorted(set(fk) | set(wk)):
+        kernels[name] = {"dispatches": [len(fk.get(name, [])), len(wk.get(name, []))],
+                         "fetch_bytes": round(med(fk[name]) / f_scale) if name in fk else 0,
+                         "write_bytes": round(med(wk[name]) / w_scale) if name in wk else 0}
+    fetch = sum(k["fetch_bytes"] for k in kernels.values())
+    write = sum(k["write_bytes"] for k in kernels.values())
+    out = {"workload": w.name, "kernel_source_hash": kernel_source_hash(), "command": command, "kernels": kernels,
+           "fetch_bytes_per_call": fetch, "write_bytes_per_call": write, "hbm_bytes_per_call": fetch + write,
            "algorithmic_bytes": alg_bytes(w.M, w.N, w.K), "copy_calibration": {"fetch": f_scale, "write": w_scale}}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
-
-
-def expected_mfma(M, N, K):
-    """Matrix instructions the product needs at 16 x 16 x 128 per
-    instruction: 16-row tiles (rows past M padded), 16-column subtiles,
-    128-wide K steps (a final 64-wide half step counted whole)."""
-    return ((M + 15) // 16) * (N // 16) * ((K + 127) // 128)
 
 
 def summarize_mfma(pmc_dir, configs, command):
@@ -290,7 +422,10 @@ def summarize_mfma(pmc_dir, configs, command):
         disp = d.setdefault(r["Dispatch_Id"], {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
         disp[r["Counter_Name"]] = float(r["Counter_Value"])
     med = lambda v: sorted(v)[len(v) // 2]
-    want = {expected_mfma(w.M, w.N, w.K): w.name for w in (syn.CONFIGS[c] for c in configs)}
+    want = {}
+    for c in configs:
+        w = syn.CONFIGS.get(c) or syn.EXTRA_SHAPES[c]
+        want[expected_mfma(w.M, w.N, w.K)] = w.name
     out = {"command": command, "kernels": []}
     for (name, grid), d in sorted(groups.items()):
         ds = list(d.values())
@@ -305,6 +440,11 @@ def summarize_mfma(pmc_dir, configs, command):
     print(json.dumps(out, indent=1))
 
 
+def workload(name):
+    import synthetic as syn
+    return syn.CONFIGS.get(name) or syn.EXTRA_SHAPES[name]
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
         summarize_pmc(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
@@ -314,13 +454,16 @@ def main():
         return
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--configs", default="c1,c2,c3,c4,c5", help="configurations measured under per_config")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--samples", type=int, default=30, help="timed replays per configuration for the statistics")
+    ap.add_argument("--configs", default="c1,c2,c3,c4,c5,p_4x2880x512,p_16x2112x7168,p_32x2880x512,p_256x3072x1536",
+                    help="configurations measured under per_config (the headline is always measured)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-b-prep", action="store_true", help="skip timing the one-launch B preparation")
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the second, warm timing (one buffer set, so inputs stay in L2 and MALL)")
+    ap.add_argument("--no-clocks", action="store_true", help="skip reading the GPU clocks with amd-smi")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="first run a cold 256 MiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -331,10 +474,13 @@ def main():
               "(N-sharding of B across GPUs needs no collective and is not implemented); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(1)
+    if args.steps < 1 or args.samples < 1:
+        print("--steps and --samples must be at least 1", file=sys.stderr)
+        sys.exit(1)
 
+    clocks_before = None if args.no_clocks else gpu_clocks()
     import torch
     import block_scaled_mxfp4_bf16_amd as mx
-    import synthetic as syn
 
     torch.cuda.set_device(0)
     if args.pmc_calibration:
@@ -344,20 +490,26 @@ def main():
         names.insert(0, HEADLINE)
     per = {}
     for name in names:
-        w = syn.CONFIGS[name]
-        r = time_config(torch, mx, w, args.steps, args.warmup, cold=True)
+        w = workload(name)
+        r = time_config(torch, mx, w, args.steps, args.warmup, args.samples, cold=True)
         if not args.no_warm:
             # context only: the same calls on one buffer set, inputs warm in L2 and MALL
-            r["warm_us_per_call"] = time_config(torch, mx, w, args.steps, args.warmup, cold=False)["us_per_call"]
+            r["warm_us_per_call"] = time_config(torch, mx, w, args.steps, args.warmup, args.samples,
+                                                cold=False)["us_per_call"]
         per[w.name] = r
-        print("[bench] %s: %.3f us/call cold%s, %.1f TFLOP/s, %.0f GB/s (%.1f%% of HBM), schedule %s"
-              % (w.name, r["us_per_call"], "" if args.no_warm else " (%.3f warm)" % r["warm_us_per_call"],
-                 r["tflops"], r["alg_gbs"], 100 * r["hbm_frac"], r["schedule"]),
+        print("[bench] %s: %.3f us/call cold (p10 %.3f, p90 %.3f%s), %.1f TFLOP/s, %.0f GB/s, %.1f%% of %s "
+              "roofline, schedule %s"
+              % (w.name, r["us_per_call"], r["us_p10"], r["us_p90"],
+                 "" if args.no_warm else "; %.3f warm" % r["warm_us_per_call"], r["tflops"], r["alg_gbs"],
+                 100 * r["roofline"]["frac"], r["roofline"]["bound"], r["schedule"]),
               file=sys.stderr, flush=True)
 
-    hw = syn.CONFIGS[HEADLINE]
+    hw = workload(HEADLINE)
     h = per[hw.name]
     print("[bench] kernel source hash %s" % kernel_source_hash(), file=sys.stderr, flush=True)
+    rl = dict(h["roofline"])
+    rl["traffic"] = measured_traffic()
+    rl["timed"] = "whole call (every launch of one mxfp4_gemm), HIP events on the replay stream"
     line = {
         "metric": "us/call and TFLOPS per (M,N,K); % of HBM or MXFP4-MFMA roofline",
         "value": h["tflops"],
@@ -365,37 +517,38 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": h["wall_ms_per_step"],
+        "ms_per_step": h["timed_us_per_call"] / 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "mxfp4 (e2m1 x e2m1 scaled MFMA, f32 accumulate, bf16 out)",
         "data": "synthetic (Philox-4x32-10 + Box-Muller N(0,1) bf16, seeded)",
-        "config": {"workload": hw.name, "M": hw.M, "N": hw.N, "K": hw.K,
-                   "cache": "cold: %d rotating buffer sets" % h["buffer_sets"], "schedule": h["schedule"]},
+        "config": {"workload": hw.name, "M": hw.M, "N": hw.N, "K": hw.K, "cache": h["cache"],
+                   "schedule": h["schedule"]},
         "us_per_call": h["us_per_call"],
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(h["alg_gbs"], 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(h["hbm_frac"], 4),
-            "traffic": measured_traffic(),
-        },
+        "us_p10": h["us_p10"],
+        "us_p90": h["us_p90"],
+        "roofline": rl,
         "per_config": per,
     }
     if not args.no_b_prep:
         # offline weight preparation (not part of a call): its own throughput
         line["b_prep"] = {}
         for name in ("c2", "c5"):
-            w = syn.CONFIGS[name]
+            w = workload(name)
             r = time_prepare_b(torch, mx, w)
             line["b_prep"][w.name] = r
             print("[bench] B prep %dx%d: %.2f us, %.0f GB/s (%.1f%% of HBM)" % (w.N, w.K, r["us_per_call"], r["gbs"],
                                                                            100 * r["hbm_frac"]),
                   file=sys.stderr, flush=True)
+    if not args.no_clocks:
+        line["clocks"] = {"before": clocks_before, "after": gpu_clocks()}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(hw)
+        threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+        line["cpu_baseline"] = cpu_baseline(threads)
+        print("[bench] oracle on the host: %.4g TFLOP/s on %d threads, %.4g on one"
+              % (line["cpu_baseline"]["value"], line["cpu_baseline"]["cores"],
+                 line["cpu_baseline"]["single_thread"]["value"]), file=sys.stderr, flush=True)
     print(json.dumps(line), flush=True)
 
 

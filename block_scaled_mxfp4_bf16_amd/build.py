@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmxfp4.so")
-SOURCES = ["mxfp4_api.hip", "quant_kernels.hip", "gemm_kernels.hip", "gemm_wide.hip"]
+SOURCES = ["mxfp4_api.hip", "quant_kernels.hip", "gemm_kernels.hip", "gemm_wide.hip"] + [
+    "gemm_table_%d.hip" % i for i in range(8)]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -1,0 +1,25 @@
+// Part 6 of the fused kernels' variant table.  The table is spread over
+// several files only so that its kernels compile in parallel; gemm_kernels.hip
+// joins the parts in order.
+#include "gemm_fused.hpp"
+
+namespace mxfp4 {
+
+static const Variant kPart[] = {
+    VQ(2, 2, 2, 1, 1), VQ(2, 2, 2, 1, 2), VQ(2, 2, 2, 1, 4), VQ(2, 2, 2, 4, 1), VQ(2, 2, 2, 4, 2), VQ(2, 2, 2, 4, 4),
+    VQ(4, 1, 1, 1, 1), VQ(4, 1, 1, 1, 2), VQ(4, 1, 1, 1, 4), VQ(4, 1, 1, 2, 1), VQ(4, 1, 1, 2, 2), VQ(4, 1, 1, 2, 4),
+    VQ(4, 1, 1, 4, 1), VQ(4, 1, 1, 4, 2), VQ(4, 1, 1, 4, 4), VQ(4, 1, 1, 8, 1), VQ(4, 1, 1, 8, 2), VQ(4, 1, 1, 8, 4),
+    VQ(4, 1, 2, 1, 1), VQ(4, 1, 2, 1, 2), VQ(4, 1, 2, 1, 4), VQ(4, 1, 2, 2, 1), VQ(4, 1, 2, 2, 2), VQ(4, 1, 2, 2, 4),
+    VQ(4, 1, 2, 4, 1), VQ(4, 1, 2, 4, 2), VQ(4, 1, 2, 4, 4), VQ(4, 1, 4, 1, 1), VQ(4, 1, 4, 1, 2), VQ(4, 1, 4, 1, 4),
+    VQ(4, 1, 4, 2, 1), VQ(4, 1, 4, 2, 2), VQ(4, 1, 4, 2, 4), VQ(4, 2, 1, 1, 1), VQ(4, 2, 1, 1, 2), VQ(4, 2, 1, 1, 4),
+    VQ(4, 2, 1, 2, 1), VQ(4, 2, 1, 2, 2), VQ(4, 2, 1, 2, 4), VQ(4, 2, 1, 4, 1), VQ(4, 2, 1, 4, 2), VQ(4, 2, 1, 4, 4),
+    VQ(4, 2, 2, 1, 1), VQ(4, 2, 2, 1, 2),
+};
+// (a host function: the device pass compiles the kernels the table names,
+// but emits no reference to the host launchers)
+const Variant *variants_part6(int *count) {
+  *count = (int)(sizeof(kPart) / sizeof(kPart[0]));
+  return kPart;
+}
+
+}  // namespace mxfp4

@@ -13,6 +13,7 @@
 
 #include "../../include/mxfp4.h"
 #include "mxfp4_internal.hpp"
+#include "workspace_pool.hpp"
 
 using namespace mxfp4;
 
@@ -317,53 +318,35 @@ mxfp4_status_t check_gemm_args(const void *A, const void *Bq, const void *Bs, co
   return MXFP4_OK;
 }
 
-// Library-owned workspaces, one per (device, stream).
-struct WsEntry {
-  int device;
-  void *stream;
-  void *ptr;
-  size_t bytes;
-};
-std::mutex g_ws_mu;
-std::vector<WsEntry> g_ws;
+// Library-owned workspaces, one per (device, stream).  A new buffer starts
+// zeroed (the split-K tickets); the fill is a kernel launch on the stream
+// that asked for it, not a memset.  Buffers replaced by larger ones stay
+// allocated (see WorkspacePool), so graphs captured before a growth keep
+// valid addresses; growth needs no synchronization.
+int alloc_workspace(int device, void *stream, size_t bytes, void **out) {
+  (void)device;  // the calling thread's current device
+  void *p = nullptr;
+  if (hipError_t e = hipMalloc(&p, bytes); e != hipSuccess) {
+    t_last_hip_error = e;
+    return MXFP4_ERR_HIP;
+  }
+  if (hipError_t e = launch_zero(p, bytes, (hipStream_t)stream); e != hipSuccess) {
+    (void)hipFree(p);
+    t_last_hip_error = e;
+    return MXFP4_ERR_HIP;
+  }
+  *out = p;
+  return MXFP4_OK;
+}
 
-// A new buffer starts zeroed (the split-K tickets); the fill is a kernel
-// launch on `stream`, not a memset.
+WorkspacePool<int (*)(int, void *, size_t, void **)> g_ws(alloc_workspace);
+
 mxfp4_status_t get_workspace(size_t need, hipStream_t stream, void **out) {
   *out = nullptr;
   if (need == 0) return MXFP4_OK;
-  need = (need + 255) & ~(size_t)255;
   int dev = 0;
   if (hipError_t e0 = hipGetDevice(&dev); e0 != hipSuccess) return hip_status(e0);
-  std::lock_guard<std::mutex> lk(g_ws_mu);
-  for (auto &e : g_ws) {
-    if (e.device == dev && e.stream == (void *)stream) {
-      if (e.bytes >= need) {
-        *out = e.ptr;
-        return MXFP4_OK;
-      }
-      // grow: wait for work that may still use the old buffer
-      if (hipError_t e0 = hipStreamSynchronize(stream); e0 != hipSuccess) return hip_status(e0);
-      if (hipError_t e0 = hipFree(e.ptr); e0 != hipSuccess) return hip_status(e0);
-      e.ptr = nullptr;
-      e.bytes = 0;
-      if (hipError_t e0 = hipMalloc(&e.ptr, need); e0 != hipSuccess) return hip_status(e0);
-      if (hipError_t e0 = launch_zero(e.ptr, need, stream); e0 != hipSuccess) return hip_status(e0);
-      e.bytes = need;
-      *out = e.ptr;
-      return MXFP4_OK;
-    }
-  }
-  WsEntry e{dev, (void *)stream, nullptr, 0};
-  if (hipError_t e0 = hipMalloc(&e.ptr, need); e0 != hipSuccess) return hip_status(e0);
-  if (hipError_t e0 = launch_zero(e.ptr, need, stream); e0 != hipSuccess) {
-    (void)hipFree(e.ptr);
-    return hip_status(e0);
-  }
-  e.bytes = need;
-  g_ws.push_back(e);
-  *out = e.ptr;
-  return MXFP4_OK;
+  return (mxfp4_status_t)g_ws.get(dev, (void *)stream, need, out);
 }
 
 bool sw_quant() {

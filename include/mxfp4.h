@@ -74,8 +74,11 @@ MXFP4_API size_t mxfp4_raw_scale_bytes(int64_t rows, int64_t K);
  * the fill submission 711914 gives its scale buffer. */
 MXFP4_API size_t mxfp4_shuffled_scale_bytes(int64_t rows, int64_t K);
 
-/* Workspace bytes mxfp4_gemm_ex needs for this shape (split-K partial sums
- * and per-tile tickets); 0 when the chosen schedule needs none. */
+/* Workspace bytes mxfp4_gemm_ex needs for this shape (split-K partial sums,
+ * per-tile tickets and, for the large-M kernel, the quantized A operand); 0
+ * when the chosen schedule needs none.  (Not on the pages: their split-K
+ * launcher allocates its partial-sum buffer per call; a C library exposes
+ * the size so the caller can own the memory.) */
 MXFP4_API size_t mxfp4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* ------------------------------------------------------------------------ */
@@ -166,8 +169,12 @@ MXFP4_API const char *mxfp4_gemm_q_schedule_name(int64_t M, int64_t N, int64_t K
 /* mxfp4_gemm uses a library-owned workspace per (device, stream), created   */
 /* on the first call for a shape that needs more (that call allocates and    */
 /* zeroes it with a fill kernel on `stream`, never a memset; later calls do  */
-/* not allocate).  The device is the calling thread's current device, which  */
-/* `stream` must belong to.  Results are deterministic: the split-K partial sums */
+/* not allocate).  A workspace that a larger one replaces is not freed: it   */
+/* stays allocated until the process ends, so a HIP graph captured before    */
+/* the growth still replays into valid memory (growth at least doubles the   */
+/* size, so what stays behind is at most about the live buffer's size).      */
+/* The device is the calling thread's current device, which `stream` must    */
+/* belong to.  Results are deterministic: the split-K partial sums */
 /* are added in a fixed order (unless an "_at" schedule is forced by         */
 /* mxfp4_set_schedule_override: its float atomics add in arrival order).     */
 /* Errors: INVALID_ARG (null, M/N/K < 1, misaligned);                        */
@@ -179,7 +186,9 @@ MXFP4_API mxfp4_status_t mxfp4_gemm(const void *A, const void *Bq_sh, const void
                           int64_t K, mxfp4_stream_t stream);
 
 /* As mxfp4_gemm with a caller-owned workspace of at least
- * mxfp4_gemm_workspace_bytes(M, N, K) bytes, 256-byte aligned.  Its first
+ * mxfp4_gemm_workspace_bytes(M, N, K) bytes, 256-byte aligned.  (Not on the
+ * pages: the caller-owned form of the workspace mxfp4_gemm keeps itself, for
+ * callers that manage memory, such as graph capture on several streams.)  Its first
  * 65536 bytes hold one ticket word per output tile and must be zero before
  * the first use (zero-fill the whole buffer once); every call leaves them at
  * zero again, so later calls -- also for other shapes -- need no clearing.
@@ -190,10 +199,13 @@ MXFP4_API mxfp4_status_t mxfp4_gemm_ex(const void *A, const void *Bq_sh, const v
                              int64_t K, void *workspace, size_t workspace_bytes, mxfp4_stream_t stream);
 
 /* Create the library-owned workspace for (M, N, K) on `stream` ahead of time
- * (so that no later mxfp4_gemm call allocates, e.g. under graph capture). */
+ * (so that no later mxfp4_gemm call allocates, e.g. under graph capture).
+ * (Not on the pages: their launchers pre-warm compiled variants; this is the
+ * same idea for the workspace.) */
 MXFP4_API mxfp4_status_t mxfp4_reserve(int64_t M, int64_t N, int64_t K, mxfp4_stream_t stream);
 
-/* Human-readable name of a status code (static storage). */
+/* Human-readable name of a status code (static storage).  (Not on the
+ * pages, whose errors are Python exceptions; the C form of their messages.) */
 MXFP4_API const char *mxfp4_status_string(mxfp4_status_t status);
 
 /* Name of the last HIP error (hipGetErrorName) that an MXFP4_ERR_HIP result */

@@ -79,31 +79,68 @@ def test_summarize_mfma_on_synthetic_counters(tmp_path, capsys):
 
 def test_summarize_pmc_scales_by_the_copy_calibration(tmp_path, monkeypatch, capsys):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
-    gemm = "void mxfp4::gemm_kernel<1, 1, 4, 1, 4, false, 16, 0>(unsigned short const*)"
+    gemm = "void mxfp4::gemm_wide_kernel<4, 7, 4, 2, false>(unsigned char const*)"
+    quant = "mxfp4::quant_quad_kernel(unsigned short const*)"
     copy = "__amd_rocclr_copyBuffer"
     cal = bench.CALIBRATION_BYTES
     # FETCH_SIZE reads half of a cold copy's bytes, WRITE_SIZE all of them (KiB per dispatch)
     fetch = [(1, 1 << 20, copy, "FETCH_SIZE", 64, 0, 1), (2, 1 << 26, copy, "FETCH_SIZE", cal / 2 / 1024, 0, 1)]
     write = [(1, 1 << 20, copy, "WRITE_SIZE", 64, 0, 1), (2, 1 << 26, copy, "WRITE_SIZE", cal / 1024, 0, 1)]
     for i, (f, w) in enumerate([(700, 256), (720, 256), (760, 256)]):
-        fetch.append((10 + i, 32768, gemm, "FETCH_SIZE", f, 0, 1))
-        write.append((10 + i, 32768, gemm, "WRITE_SIZE", w, 0, 1))
+        fetch.append((10 + 2 * i, 65536, gemm, "FETCH_SIZE", f, 0, 1))
+        write.append((10 + 2 * i, 65536, gemm, "WRITE_SIZE", w, 0, 1))
+        fetch.append((11 + 2 * i, 4096, quant, "FETCH_SIZE", 100, 0, 1))
+        write.append((11 + 2 * i, 4096, quant, "WRITE_SIZE", 30, 0, 1))
     write_counters(str(tmp_path / "f"), fetch)
     write_counters(str(tmp_path / "w"), write)
     bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), "cmd")
     out = json.loads(capsys.readouterr().out)
     assert out["copy_calibration"] == {"fetch": 0.5, "write": 1.0}
-    assert out["fetch_bytes_per_launch"] == 720 * 1024 * 2  # median, divided by the fetch scale
-    assert out["write_bytes_per_launch"] == 256 * 1024
-    assert out["hbm_bytes_per_launch"] == 720 * 2048 + 256 * 1024
-    assert out["gemm_dispatches"] == [3, 3]
+    k = out["kernels"]["void mxfp4::gemm_wide_kernel<4, 7, 4, 2, false>"]
+    assert k["fetch_bytes"] == 720 * 1024 * 2  # median, divided by the fetch scale
+    assert k["write_bytes"] == 256 * 1024 and k["dispatches"] == [3, 3]
+    assert out["fetch_bytes_per_call"] == 720 * 2048 + 100 * 2048
+    assert out["write_bytes_per_call"] == 256 * 1024 + 30 * 1024
+    assert out["hbm_bytes_per_call"] == out["fetch_bytes_per_call"] + out["write_bytes_per_call"]
     with open(tmp_path / "traffic.json") as f:
         assert json.load(f)["kernel_source_hash"] == bench.kernel_source_hash()
     # the bench reports traffic only while the hash matches the sources
-    assert bench.measured_traffic() == out["hbm_bytes_per_launch"]
+    assert bench.measured_traffic() == out["hbm_bytes_per_call"]
     with open(tmp_path / "traffic.json", "w") as f:
         json.dump(dict(out, kernel_source_hash="0" * 16), f)
     assert bench.measured_traffic() is None
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "p_4x2880x512", "p_256x3072x1536"])
+@pytest.mark.parametrize("steps", [1, 5, 20, 100, 2000])
+def test_rotation_is_cold_at_any_step_count(name, steps):
+    """A multiple of `steps` sets, at least 1 GiB of them, covered by whole
+    graphs: every call's set was last touched >= 1 GiB of other sets ago."""
+    w = bench.workload(name)
+    per = bench.set_bytes(w.M, w.N, w.K)
+    sets, graphs = bench.rotation(per, steps)
+    assert sets % steps == 0 and graphs * steps == sets
+    assert sets * per >= bench.COLD_BYTES
+    assert (sets - steps) * per < bench.COLD_BYTES or sets == steps  # no more than needed
+    assert (sets - 1) * per >= bench.COLD_BYTES - per
+
+
+def test_set_bytes_counts_the_padded_scales():
+    # N = 2112 pads to 2304 scale rows; K/32 = 224 is already a multiple of 8
+    assert bench.set_bytes(8, 2112, 7168) == 2 * 8 * 7168 + 2112 * 3584 + 2304 * 224 + 2 * 8 * 2112
+
+
+def test_percentile_and_roofline_blocks():
+    assert bench.percentile([3.0], 10) == 3.0
+    assert bench.percentile([1.0, 2.0, 3.0, 4.0, 5.0], 50) == 3.0
+    assert bench.percentile([1.0, 2.0, 3.0, 4.0, 5.0], 10) == pytest.approx(1.4)
+    r = bench.roofline(256, 7168, 7168, 10.0, "mfma")
+    assert r["unit"] == "TFLOP/s" and r["peak"] == 10100.0
+    assert r["achieved"] == pytest.approx(2 * 256 * 7168 * 7168 / 1e-5 / 1e12, abs=0.1)
+    assert r["frac"] == pytest.approx(r["achieved"] / 10100.0, abs=1e-4)
+    h = bench.roofline(32, 4096, 512, 2.0, "hbm")
+    assert h["unit"] == "GB/s" and h["achieved"] == pytest.approx(1409024 / 2e-6 / 1e9, abs=0.1)
+    assert bench.bound_of(256) == "mfma" and bench.bound_of(64) == "hbm"
 
 
 def test_more_than_one_gpu_is_refused():
