@@ -51,6 +51,7 @@ def _load():
         "mxfp4_prepare_b": (I, [P, I64, I64, P, P, P]),
         "mxfp4_gemm": (I, [P, P, P, P, I64, I64, I64, P]),
         "mxfp4_gemm_ex": (I, [P, P, P, P, I64, I64, I64, P, SZ, P]),
+        "mxfp4_gemm_noalloc": (I, [P, P, P, P, I64, I64, I64, P]),
         "mxfp4_gemm_q": (I, [P, P, P, P, P, I64, I64, I64, P]),
         "mxfp4_gemm_q_schedule_name": (ctypes.c_char_p, [I64, I64, I64]),
         "mxfp4_reserve": (I, [I64, I64, I64, P]),
@@ -77,7 +78,7 @@ def exported_symbols():
     """Names every entry point the header declares (used by the ABI test)."""
     return ["mxfp4_packed_bytes", "mxfp4_raw_scale_bytes", "mxfp4_shuffled_scale_bytes",
             "mxfp4_gemm_workspace_bytes", "mxfp4_quantize", "mxfp4_preshuffle_b", "mxfp4_prepare_b", "mxfp4_gemm",
-            "mxfp4_gemm_ex", "mxfp4_gemm_q", "mxfp4_gemm_q_schedule_name", "mxfp4_reserve", "mxfp4_status_string", "mxfp4_last_hip_error", "mxfp4_gemm_schedule_name",
+            "mxfp4_gemm_ex", "mxfp4_gemm_noalloc", "mxfp4_gemm_q", "mxfp4_gemm_q_schedule_name", "mxfp4_reserve", "mxfp4_status_string", "mxfp4_last_hip_error", "mxfp4_gemm_schedule_name",
             "mxfp4_set_quant_mode", "mxfp4_set_schedule_override", "mxfp4_list_schedules"]
 
 
@@ -154,6 +155,11 @@ def mxfp4_gemm(A, Bq_sh, Bs_sh, C, M: int, N: int, K: int, stream=None):
 def mxfp4_gemm_ex(A, Bq_sh, Bs_sh, C, M: int, N: int, K: int, workspace, workspace_bytes: int, stream=None):
     _check(_load().mxfp4_gemm_ex(_ptr(A), _ptr(Bq_sh), _ptr(Bs_sh), _ptr(C), M, N, K, _ptr(workspace),
                                  workspace_bytes, _stream(stream)), "mxfp4_gemm_ex")
+
+
+def mxfp4_gemm_noalloc(A, Bq_sh, Bs_sh, C, M: int, N: int, K: int, stream=None):
+    _check(_load().mxfp4_gemm_noalloc(_ptr(A), _ptr(Bq_sh), _ptr(Bs_sh), _ptr(C), M, N, K, _stream(stream)),
+           "mxfp4_gemm_noalloc")
 
 
 def mxfp4_gemm_q(Aq, As, Bq_sh, Bs_sh, C, M: int, N: int, K: int, stream=None):

@@ -349,6 +349,36 @@ mxfp4_status_t get_workspace(size_t need, hipStream_t stream, void **out) {
   return (mxfp4_status_t)g_ws.get(dev, (void *)stream, need, out);
 }
 
+// Scratch of mxfp4_gemm_noalloc: a file-scope device array, one copy per
+// GPU, held until the process ends.  Host code never uses its name as an
+// address: the first call on a device looks the device copy's address up
+// with hipGetSymbolAddress (with that device current) and keeps it, and
+// every later use goes through the kept pointer.
+static __device__ __align__(256) uint8_t scratch[MXFP4_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch; on the first call for a device its ticket
+// prefix is cleared with a fill kernel on `stream` (no memset, no
+// allocation).
+mxfp4_status_t scratch_of_current_device(hipStream_t stream, void **out) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MXFP4_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess) return hip_status(e);
+    if (!p) return hip_status(hipErrorInvalidSymbol);
+    if (hipError_t e = launch_zero(p, kTicketBytes, stream); e != hipSuccess) return hip_status(e);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MXFP4_OK;
+}
+
 bool sw_quant() {
   std::lock_guard<std::mutex> lk(g_opt_mu);
   return g_quant_mode == 1;
@@ -474,6 +504,23 @@ mxfp4_status_t mxfp4_gemm(const void *A, const void *Bq_sh, const void *Bs_sh, v
   void *ws = nullptr;
   st = get_workspace(need, (hipStream_t)stream, &ws);
   if (st != MXFP4_OK) return st;
+  GemmArgs a{A, Bq_sh, Bs_sh, C, ws, (int)M, (int)N, (int)K};
+  return hip_status(launch_gemm(s, a, sw_quant(), (hipStream_t)stream));
+}
+
+mxfp4_status_t mxfp4_gemm_noalloc(const void *A, const void *Bq_sh, const void *Bs_sh, void *C, int64_t M, int64_t N,
+                                  int64_t K, mxfp4_stream_t stream) {
+  mxfp4_status_t st = check_gemm_args(A, Bq_sh, Bs_sh, C, M, N, K);
+  if (st != MXFP4_OK) return st;
+  Schedule s;
+  if (!choose((int)M, (int)N, (int)K, &s)) return MXFP4_ERR_UNSUPPORTED;
+  const size_t need = gemm_workspace_bytes(s, (int)M, (int)N, (int)K);
+  if (need > (size_t)MXFP4_NOALLOC_SCRATCH_BYTES) return MXFP4_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if (need > 0) {
+    st = scratch_of_current_device((hipStream_t)stream, &ws);
+    if (st != MXFP4_OK) return st;
+  }
   GemmArgs a{A, Bq_sh, Bs_sh, C, ws, (int)M, (int)N, (int)K};
   return hip_status(launch_gemm(s, a, sw_quant(), (hipStream_t)stream));
 }

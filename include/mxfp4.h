@@ -198,6 +198,27 @@ MXFP4_API mxfp4_status_t mxfp4_gemm(const void *A, const void *Bq_sh, const void
 MXFP4_API mxfp4_status_t mxfp4_gemm_ex(const void *A, const void *Bq_sh, const void *Bs_sh, void *C, int64_t M, int64_t N,
                              int64_t K, void *workspace, size_t workspace_bytes, mxfp4_stream_t stream);
 
+/* ------------------------------------------------------------------------ */
+/* mxfp4_gemm without any allocation, for callers that cannot allocate:     */
+/* code under HIP graph capture, tight serving loops, harnesses that forbid */
+/* hipMalloc.  Same arguments, results and errors as mxfp4_gemm.  Instead of */
+/* a workspace it uses a scratch array of MXFP4_NOALLOC_SCRATCH_BYTES that  */
+/* the library holds in device memory, one per GPU, from the first call on  */
+/* that GPU until the process ends.  It calls no hipMalloc, hipFree or       */
+/* other allocating routine; the first call on a GPU looks the array up and  */
+/* clears its ticket words with a fill kernel on `stream`.                   */
+/* Every call on a GPU shares that GPU's array, which keeps the last call's  */
+/* contents: calls that overlap in time on one GPU (concurrent streams,      */
+/* threads) race and must be serialized by the caller.                       */
+/* Errors: as mxfp4_gemm, plus WORKSPACE when the schedule chosen for the    */
+/* shape needs more than MXFP4_NOALLOC_SCRATCH_BYTES (large M times long K:  */
+/* the quantized A operand of the large-M kernel, about M * K * 17/32 bytes, */
+/* or split-K partial sums).                                                 */
+/* ------------------------------------------------------------------------ */
+#define MXFP4_NOALLOC_SCRATCH_BYTES (8 * 1024 * 1024)
+MXFP4_API mxfp4_status_t mxfp4_gemm_noalloc(const void *A, const void *Bq_sh, const void *Bs_sh, void *C, int64_t M,
+                                            int64_t N, int64_t K, mxfp4_stream_t stream);
+
 /* Create the library-owned workspace for (M, N, K) on `stream` ahead of time
  * (so that no later mxfp4_gemm call allocates, e.g. under graph capture).
  * (Not on the pages: their launchers pre-warm compiled variants; this is the

@@ -8,6 +8,7 @@ import re
 import pytest
 
 import block_scaled_mxfp4_bf16_amd as mx
+import synthetic as syn
 from tests.conftest import ROOT
 
 HEADER = os.path.join(ROOT, "include", "mxfp4.h")
@@ -70,6 +71,20 @@ def test_gemm_rejects_bad_arguments(args, code):
     L = mx.lib()
     assert L.mxfp4_gemm(*args, None) == code
     assert L.mxfp4_gemm_ex(*args, None, 0, None) == code
+    assert L.mxfp4_gemm_noalloc(*args, None) == code
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    """The no-allocation entry point checks the chosen schedule's workspace
+    against its fixed scratch size on the host, before any HIP call."""
+    L = mx.lib()
+    limit = 8 * 1024 * 1024
+    M, N, K = 4096, 4096, 8192  # large-M kernel: its quantized A operand alone is ~17 MB
+    assert mx.mxfp4_gemm_workspace_bytes(M, N, K) > limit
+    assert L.mxfp4_gemm_noalloc(FAKE, FAKE, FAKE, FAKE, M, N, K, None) == WORKSPACE
+    # the benchmark shapes all fit
+    for w in list(syn.CONFIGS.values()) + list(syn.EXTRA_SHAPES.values()):
+        assert mx.mxfp4_gemm_workspace_bytes(w.M, w.N, w.K) <= limit, w.name
 
 
 def test_gemm_ex_rejects_small_workspace():
