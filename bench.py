@@ -155,15 +155,26 @@ def measured_traffic():
 
 
 def gpu_clocks():
-    """Current GPU clocks as amd-smi reports them (JSON), or the error."""
+    """Current GPU clocks as amd-smi reports them: MHz per clock domain
+    (gfx_0..7 are the eight XCDs' shader clocks), or the error."""
     try:
         r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
                            timeout=30)
         if r.returncode != 0:
             return {"error": (r.stderr or r.stdout).strip()[-300:]}
-        return json.loads(r.stdout)
+        return compact_clocks(json.loads(r.stdout))
     except Exception as e:  # the clocks are context; the measurement does not depend on them
         return {"error": repr(e)[-300:]}
+
+
+def compact_clocks(d):
+    """{domain: MHz} from amd-smi's JSON (a list of GPUs, or one GPU)."""
+    g = d["gpu_data"][0] if isinstance(d, dict) and "gpu_data" in d else (d[0] if isinstance(d, list) else d)
+    out = {}
+    for name, v in g.get("clock", {}).items():
+        if isinstance(v, dict) and isinstance(v.get("clk"), dict):
+            out[name] = v["clk"].get("value")
+    return out
 
 
 def cpu_model():
@@ -194,10 +205,13 @@ def prepare(torch, mx, w, sets):
     return out
 
 
-def time_config(torch, mx, w, steps, warmup, samples, cold=True):
+def time_config(torch, mx, w, steps, warmup, samples, cold=True, clocks_under_load=False):
     """Time `steps`-call graph replays of the workload (see the module
     docstring).  Returns the per-call figures of the first timed replay (the
-    contract's timed region) and the statistics over `samples` replays."""
+    contract's timed region) and the statistics over `samples` replays.
+    With clocks_under_load, the replays then go on (untimed) while amd-smi
+    reads the clocks from another thread, so the reading is taken under this
+    workload's load rather than at idle."""
     M, N, K = w.M, w.N, w.K
     per_set = set_bytes(M, N, K)
     sets, graphs = rotation(per_set, steps) if cold else (1, 1)
@@ -241,6 +255,29 @@ def time_config(torch, mx, w, steps, warmup, samples, cold=True):
             ev[s][1].record(stream)
     torch.cuda.synchronize()
     us = [a.elapsed_time(b) * 1e3 / steps for a, b in ev]
+    load_clocks = None
+    if clocks_under_load:
+        import threading
+        box = {}
+        t = threading.Thread(target=lambda: box.setdefault("c", gpu_clocks()))
+        t0 = time.perf_counter()
+        k = 0
+        with torch.cuda.stream(stream):
+            # a second of continuous load first (the clock readings are
+            # averaged over a window), then more while amd-smi runs (bounded)
+            while time.perf_counter() - t0 < 1.0:
+                for _ in range(20):
+                    gs[k % graphs].replay()
+                    k += 1
+                stream.synchronize()
+            t.start()
+            while t.is_alive() and time.perf_counter() - t0 < 30:
+                for _ in range(20):
+                    gs[k % graphs].replay()
+                    k += 1
+                stream.synchronize()
+        t.join()
+        load_clocks = dict(box.get("c") or {}, replays=k, seconds=round(time.perf_counter() - t0, 2))
     del gs, bufs
     torch.cuda.empty_cache()
     med = percentile(us, 50)
@@ -263,6 +300,8 @@ def time_config(torch, mx, w, steps, warmup, samples, cold=True):
         "mfma_frac": alg_flops(M, N, K) / (med * 1e-6) / 1e12 / FP4_PEAK_TFLOPS,
     }
     r["roofline"] = roofline(M, N, K, med, bound_of(M))
+    if load_clocks is not None:
+        r["clocks_under_load"] = load_clocks
     return r
 
 
@@ -491,7 +530,8 @@ def main():
     per = {}
     for name in names:
         w = workload(name)
-        r = time_config(torch, mx, w, args.steps, args.warmup, args.samples, cold=True)
+        r = time_config(torch, mx, w, args.steps, args.warmup, args.samples, cold=True,
+                        clocks_under_load=(name == HEADLINE and not args.no_clocks))
         if not args.no_warm:
             # context only: the same calls on one buffer set, inputs warm in L2 and MALL
             r["warm_us_per_call"] = time_config(torch, mx, w, args.steps, args.warmup, args.samples,
@@ -542,7 +582,8 @@ def main():
                                                                            100 * r["hbm_frac"]),
                   file=sys.stderr, flush=True)
     if not args.no_clocks:
-        line["clocks"] = {"before": clocks_before, "after": gpu_clocks()}
+        line["clocks"] = {"before": clocks_before, "under_headline_load": h.get("clocks_under_load"),
+                          "after": gpu_clocks()}
     if not args.no_cpu_baseline:
         threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
         line["cpu_baseline"] = cpu_baseline(threads)
