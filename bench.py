@@ -479,6 +479,97 @@ def summarize_mfma(pmc_dir, configs, command):
     print(json.dumps(out, indent=1))
 
 
+PROBES_LIB = os.path.join(ROOT, "block_scaled_mxfp4_bf16_amd", "libmxfp4_probes.so")
+
+
+def floors(torch, steps, samples, names):
+    """Floors of this machine, measured with the probe library: one launch of
+    an empty kernel; the least time to stream each workload's B (codes and
+    padded scales) from memory in one launch of plain coalesced loads (cold
+    rotation as for the GEMM, the best of several grid sizes); and the
+    scaled FP4 matrix instructions' issue rate with the shader clock
+    (s_memtime against the 100 MHz s_memrealtime) measured alongside.
+    All timed as graph replays of `steps` launches, median over `samples`."""
+    import ctypes
+    L = ctypes.CDLL(PROBES_LIB)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    L.mxfp4_probe_empty.argtypes = [P]
+    L.mxfp4_probe_stream.argtypes = [P, ctypes.c_size_t, P, I, P]
+    L.mxfp4_probe_mfma.argtypes = [P, P, I, I, P]
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+
+    def graph_time(call, count):
+        gs = []
+        for j in range(count):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(steps):
+                    call(j * steps + i)
+            gs.append(g)
+        with torch.cuda.stream(stream):
+            for g in gs:
+                g.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
+        with torch.cuda.stream(stream):
+            for k in range(samples):
+                ev[k][0].record(stream)
+                gs[k % count].replay()
+                ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        us = [a.elapsed_time(b) * 1e3 / steps for a, b in ev]
+        return percentile(us, 50), percentile(us, 10), percentile(us, 90)
+
+    out = {}
+    med, p10, p90 = graph_time(lambda i: L.mxfp4_probe_empty(sh), 1)
+    out["empty_kernel_us"] = {"median": round(med, 3), "p10": round(p10, 3), "p90": round(p90, 3)}
+    print("[floors] empty kernel: %.3f us per launch" % med, file=sys.stderr, flush=True)
+    sink = torch.empty(8192 * 256, dtype=torch.int32, device="cuda")
+    out["stream_b_us"] = {}
+    for name in names:
+        w = workload(name)
+        nbytes = w.N * w.K // 2 + ((w.N + 255) // 256 * 256) * ((w.K // 32 + 7) // 8 * 8)
+        nbytes = (nbytes + 15) // 16 * 16
+        sets, graphs = rotation(nbytes, steps)
+        bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(sets)]
+        best = None
+        for wgs in (256, 512, 1024, 2048):
+            if wgs * 256 * 16 > nbytes * 4:
+                continue
+            med, p10, p90 = graph_time(
+                lambda i, wgs=wgs: L.mxfp4_probe_stream(bufs[i % sets].data_ptr(), nbytes, sink.data_ptr(), wgs, sh),
+                graphs)
+            if best is None or med < best[0]:
+                best = (med, wgs)
+        del bufs
+        torch.cuda.empty_cache()
+        out["stream_b_us"][w.name] = {"bytes": nbytes, "us": round(best[0], 3), "workgroups": best[1],
+                                      "gbs": round(nbytes / (best[0] * 1e-6) / 1e9, 1)}
+        print("[floors] stream %s B (%d bytes): %.3f us (%d workgroups)" % (w.name, nbytes, best[0], best[1]),
+              file=sys.stderr, flush=True)
+    out["mfma"] = []
+    for wgs, iters in ((256, 4096), (1024, 1024)):
+        o = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+        st = torch.zeros(wgs * 4, dtype=torch.int64, device="cuda")
+        med, p10, p90 = graph_time(lambda i: L.mxfp4_probe_mfma(o.data_ptr(), st.data_ptr(), wgs, iters, sh), 1)
+        t = st.view(wgs, 4).cpu().tolist()
+        ticks = sorted(r[1] - r[0] for r in t)[wgs // 2]
+        real = sorted(r[3] - r[2] for r in t)[wgs // 2]
+        inst = wgs * 4 * iters * 8
+        flops = inst * 65536
+        out["mfma"].append({
+            "workgroups": wgs, "waves_per_simd": wgs // 256, "instructions": inst, "us": round(med, 3),
+            "tflops": round(flops / (med * 1e-6) / 1e12, 1),
+            "shader_mhz": round(ticks / real * 100.0, 1) if real else None,
+            "cycles_per_instruction_per_wave": round(ticks / (iters * 8), 2)})
+        print("[floors] MFMA %d workgroups: %.3f us, %.0f TFLOP/s, shader clock %s MHz, %.2f cycles per "
+              "instruction per wave" % (wgs, med, flops / (med * 1e-6) / 1e12, out["mfma"][-1]["shader_mhz"],
+                                        out["mfma"][-1]["cycles_per_instruction_per_wave"]),
+              file=sys.stderr, flush=True)
+    return out
+
+
 def workload(name):
     import synthetic as syn
     return syn.CONFIGS.get(name) or syn.EXTRA_SHAPES[name]
@@ -503,6 +594,9 @@ def main():
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the second, warm timing (one buffer set, so inputs stay in L2 and MALL)")
     ap.add_argument("--no-clocks", action="store_true", help="skip reading the GPU clocks with amd-smi")
+    ap.add_argument("--floors", action="store_true",
+                    help="measure the machine's floors with the probe library instead (launch, B streaming, "
+                         "matrix-instruction rate and clock) and print them as one JSON line")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="first run a cold 256 MiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -522,6 +616,11 @@ def main():
     import block_scaled_mxfp4_bf16_amd as mx
 
     torch.cuda.set_device(0)
+    if args.floors:
+        names = [c for c in args.configs.split(",") if c]
+        print(json.dumps({"floors": floors(torch, args.steps, args.samples, names), "steps": args.steps,
+                          "samples": args.samples, "clocks": clocks_before}), flush=True)
+        return
     if args.pmc_calibration:
         calibration_copy(torch)
     names = [c for c in args.configs.split(",") if c]

@@ -9,6 +9,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmxfp4.so")
+# Measurement probes for bench.py --floors (a library of their own: nothing
+# in libmxfp4.so uses them).
+PROBES_SRC = "probes.hip"
+PROBES_LIB = os.path.join(PKG, "libmxfp4_probes.so")
 SOURCES = ["mxfp4_api.hip", "quant_kernels.hip", "gemm_kernels.hip", "gemm_wide.hip"] + [
     "gemm_table_%d.hip" % i for i in range(8)]
 ARCH = "gfx950"
@@ -31,7 +35,7 @@ HIPCC_FLAGS = [
 # result is tied to its accumulator input when the accumulator lives in
 # AGPRs, so long accumulation loops get copies between every pair of
 # instructions; keeping accumulators in VGPRs lets them update in place.
-EXTRA_FLAGS = {"gemm_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA_FLAGS = {"gemm_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "probes.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -65,6 +69,14 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             sys.stderr.write(text)
         elif verbose and lines:
             sys.stderr.write("\n".join(lines) + "\n")
+    probe_cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS[PROBES_SRC], "-shared", "-o", PROBES_LIB + ".tmp%d" % os.getpid(),
+                 os.path.join(CSRC, PROBES_SRC)]
+    pp = subprocess.run(probe_cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if pp.returncode != 0:
+        failed.append(PROBES_SRC)
+        sys.stderr.write(pp.stdout.decode(errors="replace"))
+    else:
+        os.replace(PROBES_LIB + ".tmp%d" % os.getpid(), PROBES_LIB)
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
     tmp = LIB + ".tmp%d" % os.getpid()

@@ -42,44 +42,56 @@ size_t quad_operand_bytes(int M, int K) {
   return mq * ks * (4 * 1024 + 256);
 }
 
-// One single-wave workgroup per (16-row tile, K step): 16 rows x 128
-// elements of bf16 A, in four coalesced 16-byte loads per lane (each covers
-// the 16 rows x one 32-element group, four lanes per group, as in the fused
-// kernels' staging).  Small units spread the work over many CUs: each CU's
-// intake from HBM, not the arithmetic, bounds this kernel.  The tile's
-// scale bytes go to byte j = t % 4 of the quad's scale dwords.  Rows past M
-// and chunks past K load as zeros and are written as zero codes with scale
-// byte 0; the tiles of the last quad past M are written the same way.
-__global__ __launch_bounds__(64) void quant_quad_kernel(const uint16_t *__restrict__ A, uint8_t *__restrict__ Aop,
-                                                        int M, int K, int units, int sw_quant) {
-  const int lane = threadIdx.x;
-  const int unit = blockIdx.x;
-  if (unit >= units) return;
+// One two-wave workgroup per (tile quad q, K step ks): wave h quantizes
+// tiles 4q + 2h and 4q + 2h + 1, each 16 rows x 128 elements of bf16 A in
+// four coalesced 16-byte loads per lane (one per 32-element group, four
+// lanes per group, as in the fused kernels' staging).  All eight loads of a
+// lane are issued before any is used, so a workgroup pays one memory round
+// trip, and the grid (one workgroup per quad and step) spreads A over the
+// CUs.  Codes go to the tiles' 1 KiB blocks; the two tiles' scale bytes of
+// an operand lane go to half h of that lane's scale dword as one 16-bit
+// store.  Rows past M and chunks past K load as zeros and are written as
+// zero codes with scale byte 0; so are the tiles of the last quad past M.
+__global__ __launch_bounds__(128) void quant_quad_kernel(const uint16_t *__restrict__ A, uint8_t *__restrict__ Aop,
+                                                         int M, int K, int sw_quant) {
+  const int lane = threadIdx.x & 63;
+  const int h = threadIdx.x >> 6;
   const int KS = (K + 127) >> 7;
-  const int ks = unit % KS;
-  const int t = unit / KS;  // 16-row tile
+  const int q = blockIdx.x / KS;
+  const int ks = blockIdx.x - q * KS;
   const int mq = (M + 63) >> 6;
   const int a_bytes = M * K * 2;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, a_bytes, kRsrcWord3);
-  u32x4 w[4];
-  const int row = t * 16 + (lane >> 2);
+  u32x4 w[2][4];
 #pragma unroll
-  for (int ch = 0; ch < 4; ++ch) {
-    const int kel = ks * 128 + ch * 32 + (lane & 3) * 8;
-    const bool ok = (row < M) && (ks * 128 + ch * 32 < K);
-    w[ch] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off_or_oob(ok, (row * K + kel) * 2), 0, 0);
-  }
-  uint32_t *codes = (uint32_t *)Aop;
-  uint8_t *scales = Aop + (size_t)mq * 4 * KS * 1024;
-  auto run = [&](auto sw_tag) {
-    constexpr bool SW = decltype(sw_tag)::value;
+  for (int j = 0; j < 2; ++j) {
+    const int row = (4 * q + 2 * h + j) * 16 + (lane >> 2);
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
-      uint32_t s;
-      const uint32_t d = quant_quarter_t<SW>(w[ch], &s);
-      // lane = 4*row + quarter: dword (16*ch + row)*4 + quarter of the block
-      codes[(size_t)(t * KS + ks) * 256 + ch * 64 + lane] = d;
-      if ((lane & 3) == 0) scales[((size_t)((t >> 2) * KS + ks) * 64 + ch * 16 + (lane >> 2)) * 4 + (t & 3)] = (uint8_t)s;
+      const int kel = ks * 128 + ch * 32 + (lane & 3) * 8;
+      const bool ok = (row < M) && (ks * 128 + ch * 32 < K);
+      w[j][ch] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off_or_oob(ok, (row * K + kel) * 2), 0, 0);
+    }
+  }
+  uint32_t *codes = (uint32_t *)Aop;
+  uint16_t *scales = (uint16_t *)(Aop + (size_t)mq * 4 * KS * 1024);
+  auto run = [&](auto sw_tag) {
+    constexpr bool SW = decltype(sw_tag)::value;
+    uint32_t s[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int t = 4 * q + 2 * h + j;
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) {
+        // lane = 4*row + quarter: dword (16*ch + row)*4 + quarter of the block
+        codes[(size_t)(t * KS + ks) * 256 + ch * 64 + lane] = quant_quarter_t<SW>(w[j][ch], &s[j][ch]);
+      }
+    }
+    // operand lane 16*ch + row: bytes 2h, 2h + 1 of its dword
+    if ((lane & 3) == 0) {
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch)
+        scales[((size_t)(q * KS + ks) * 64 + ch * 16 + (lane >> 2)) * 2 + h] = (uint16_t)(s[0][ch] | (s[1][ch] << 8));
     }
   };
   if (sw_quant)
@@ -504,11 +516,11 @@ template <int MW, int NW, int W, int D, bool BL>
 static hipError_t launch_wide(const GemmArgs &a, int split, bool sw, hipStream_t stream) {
   char *ws = (char *)a.workspace;
   uint8_t *aop = (uint8_t *)(ws + kTicketBytes);
-  const int units = ((a.M + 63) / 64) * ((a.K + 127) / 128);
+  const int units = ((a.M + 63) / 64) * ((a.K + 127) / 128);  // (tile quad, K step)
   if (a.Aq)
     repack_quad_kernel<<<units, 64, 0, stream>>>((const uint8_t *)a.Aq, (const uint8_t *)a.As, aop, a.M, a.K);
   else
-    quant_quad_kernel<<<units * 4, 64, 0, stream>>>((const uint16_t *)a.A, aop, a.M, a.K, units * 4, sw ? 1 : 0);
+    quant_quad_kernel<<<units, 128, 0, stream>>>((const uint16_t *)a.A, aop, a.M, a.K, sw ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_tiles = a.N / (16 * NW);
