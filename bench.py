@@ -14,11 +14,13 @@ were last read >= 1 GiB of other traffic ago and come from HBM.  The calls
 are captured as S / steps HIP graphs of --steps calls each, replayed in turn
 so the rotation continues from one replay to the next.
 
-Timed region: one replay of the next graph (exactly --steps calls, each on
+Timed region: one replay of the first graph (exactly --steps calls, each on
 its own set), bracketed by device synchronizations, with HIP events recorded
 on the replay stream; ms_per_step is that replay's event time / steps.
-Statistics: further replays (the rotation continuing), each timed by events,
-give the median, p10 and p90 of the time per call.
+Statistics: one more graph holds whole rotations (every set in order, at
+least 200 calls), so that the cost of launching a graph is spread as it is
+over a long run of calls; --samples replays of it, each timed by events,
+give the median, p10 and p90 of the time per call (us_per_call, value).
 
 The headline is the largest configuration, M=256 N=7168 K=7168, reported as
 TFLOP/s against the dense MXFP4 matrix peak.  Every configuration (the five
@@ -237,24 +239,37 @@ def time_config(torch, mx, w, steps, warmup, samples, cold=True, clocks_under_lo
             g.replay()  # the first replay of a graph uploads it
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
     # the timed region: one replay, exactly `steps` calls
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
-        ev[0][0].record(stream)
+        e0.record(stream)
         gs[0].replay()
-        ev[0][1].record(stream)
+        e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # statistics: the rotation continues through the graphs in order
+    timed_us = e0.elapsed_time(e1) * 1e3 / steps
+    # statistics: a graph of whole rotations, continuing after graph 0
+    rounds = max(1, math.ceil(200 / sets))
+    long_calls = rounds * sets
+    lg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(lg, stream=stream):
+        for i in range(long_calls):
+            A, Bw, Bs, C = bufs[(steps + i) % sets]
+            mx.mxfp4_gemm(A, Bw, Bs, C, M, N, K, stream=stream)
     with torch.cuda.stream(stream):
-        for s in range(1, samples):
+        lg.replay()  # upload
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
+    with torch.cuda.stream(stream):
+        for s in range(samples):
             ev[s][0].record(stream)
-            gs[s % graphs].replay()
+            lg.replay()
             ev[s][1].record(stream)
     torch.cuda.synchronize()
-    us = [a.elapsed_time(b) * 1e3 / steps for a, b in ev]
+    us = [a.elapsed_time(b) * 1e3 / long_calls for a, b in ev]
+    del lg
     load_clocks = None
     if clocks_under_load:
         import threading
@@ -288,9 +303,9 @@ def time_config(torch, mx, w, steps, warmup, samples, cold=True, clocks_under_lo
                   "calls earlier" % (sets, per_set, sets * per_set / 2 ** 30, sets)) if cold else
                  "warm: one buffer set (inputs resident in L2 and MALL)",
         "buffer_sets": sets, "set_bytes": per_set, "footprint_bytes": sets * per_set,
-        "timed_us_per_call": round(us[0], 4),
+        "timed_us_per_call": round(timed_us, 4),
         "timed_wall_ms": round(wall * 1e3, 4),
-        "samples": samples, "calls_per_sample": steps,
+        "samples": samples, "calls_per_sample": long_calls,
         "us_per_call": round(med, 4),
         "us_p10": round(percentile(us, 10), 4), "us_p90": round(percentile(us, 90), 4),
         "us_min": round(min(us), 4), "us_max": round(max(us), 4),

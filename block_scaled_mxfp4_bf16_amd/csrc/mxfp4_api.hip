@@ -81,7 +81,7 @@ const Tuned kTuned[] = {
     {64, 7168, 2048, "mt1_nt2_wn4_wk4_kpw4_split1"},
     {256, 7168, 7168, "wide_mt4_nt7_w4_d2_split1"},
     // the leaderboard's other shapes
-    {4, 2880, 512, "mt1_nt1_wn1_wk4_kpw1_split1_r8"},
+    {4, 2880, 512, "mt1_nt2_wn1_wk4_kpw1_split1"},
     {16, 2112, 7168, "mt1_nt1_wn4_wk4_kpw4_split4"},
     {32, 2880, 512, "mt1_nt1_wn4_wk1_kpw4_split1"},
     {256, 3072, 1536, "mt1_nt2_wn8_wk2_kpw8_split1"},

@@ -1,13 +1,14 @@
 """Time every compiled schedule that can serve a GEMM shape, on the GPU.
 
-    python -m block_scaled_mxfp4_bf16_amd.tune 32x4096x512 [MxNxK ...] [--steps 200] [--top 10]
+    python -m block_scaled_mxfp4_bf16_amd.tune 32x4096x512 [MxNxK ...] [--steps 50] [--top 10]
                                              [--confirm 3] [--json out.json] [--quantized-a]
 
 For each shape: random bf16 A and B (B prepared with mxfp4_prepare_b), then
-for each name from mxfp4_list_schedules, `steps` calls captured in a HIP
-graph and replayed between events.  Calls cycle through enough copies of
-(A, B, scales, C) -- at least 1 GiB -- that every call reads its inputs from
-HBM, as a call in a real workload would.  The best `top` are then re-timed
+for each name from mxfp4_list_schedules, the calls are captured in HIP graphs
+of `steps` calls and a full pass over them is replayed between events.  The
+calls cycle, in order, through a multiple of `steps` copies of (A, B, scales,
+C) totalling at least 1 GiB (4x the MALL), so every call reads its inputs
+from HBM, as a call in a real workload would.  The best `top` are then re-timed
 `confirm` times in alternation, with the built-in choice among them, so that
 drift over the run cannot decide the ranking.  Pin the winner with
 mxfp4_set_schedule_override(name).
@@ -22,7 +23,7 @@ import torch
 import block_scaled_mxfp4_bf16_amd as mx
 
 
-def prepare(M, N, K, quantized_a, seed=0):
+def prepare(M, N, K, quantized_a, steps, seed=0):
     g = torch.Generator(device="cuda").manual_seed(seed)
     a = torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16)
     b = torch.randn((N, K), generator=g, device="cuda").to(torch.bfloat16)
@@ -36,7 +37,8 @@ def prepare(M, N, K, quantized_a, seed=0):
         a_in = (a,)
         a_bytes = 2 * M * K
     per_set = a_bytes + bw.numel() + bs.numel() + 2 * M * N
-    sets = min(512, max(2, math.ceil((1 << 30) / per_set)))
+    need = math.ceil((1 << 30) / per_set)
+    sets = steps * math.ceil(need / steps)
     bufs = []
     for i in range(sets):
         clone = (lambda t: t) if i == 0 else (lambda t: t.clone())
@@ -64,31 +66,36 @@ def time_schedule(M, N, K, quantized_a, bufs, stream, name, steps):
             for i in range(3):
                 call(M, N, K, quantized_a, bufs[i % len(bufs)], stream)
         stream.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(steps):
-                call(M, N, K, quantized_a, bufs[i % len(bufs)], stream)
+        gs = []
+        for j in range(len(bufs) // steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(steps):
+                    call(M, N, K, quantized_a, bufs[j * steps + i], stream)
+            gs.append(g)
         with torch.cuda.stream(stream):
-            g.replay()  # the first replay uploads the graph
+            for g in gs:
+                g.replay()  # the first replay uploads the graph
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
             e0.record(stream)
-            g.replay()
+            for g in gs:
+                g.replay()  # every set once, in order
             e1.record(stream)
         torch.cuda.synchronize()
-        del g
-        return e0.elapsed_time(e1) * 1e3 / steps
+        del gs
+        return e0.elapsed_time(e1) * 1e3 / len(bufs)
     finally:
         mx.mxfp4_set_schedule_override(None)
 
 
-def tune(M, N, K, quantized_a=False, steps=200, top=10, confirm=3, log=print):
+def tune(M, N, K, quantized_a=False, steps=50, top=10, confirm=3, log=print):
     names = mx.mxfp4_list_schedules(M, N, K, quantized_a)
     if not names:
         raise ValueError("no schedule serves %dx%dx%d" % (M, N, K))
     builtin = (mx.mxfp4_gemm_q_schedule_name if quantized_a else mx.mxfp4_gemm_schedule_name)(M, N, K)
-    bufs = prepare(M, N, K, quantized_a)
+    bufs = prepare(M, N, K, quantized_a, steps)
     stream = torch.cuda.Stream()
     times = {}
     for i, n in enumerate(names):
@@ -100,7 +107,7 @@ def tune(M, N, K, quantized_a=False, steps=200, top=10, confirm=3, log=print):
     again = {n: [] for n in finalists}
     for _ in range(confirm):
         for n in finalists:
-            again[n].append(time_schedule(M, N, K, quantized_a, bufs, stream, n, 2 * steps))
+            again[n].append(time_schedule(M, N, K, quantized_a, bufs, stream, n, steps))
     final = sorted(finalists, key=lambda n: sum(again[n]) / len(again[n]))
     res = {"shape": [M, N, K], "quantized_a": bool(quantized_a), "builtin": builtin, "times_us": times,
            "confirmed_us": {n: sum(v) / len(v) for n, v in again.items()}, "best": final[0]}
@@ -118,7 +125,7 @@ def tune(M, N, K, quantized_a=False, steps=200, top=10, confirm=3, log=print):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("shapes", nargs="+", help="MxNxK")
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=50, help="calls per graph (the sets are a multiple of this)")
     ap.add_argument("--top", type=int, default=10)
     ap.add_argument("--confirm", type=int, default=3)
     ap.add_argument("--quantized-a", action="store_true", help="time mxfp4_gemm_q (A given as codes and scales)")
