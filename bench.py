@@ -435,16 +435,20 @@ def summarize_pmc(fetch_dir, write_dir, command):
             if "mxfp4::" in name:
                 kern.setdefault(name.split("(")[0], []).append(v)
             elif "copyBuffer" in name:
-                copy.append((int(r["Grid_Size"]), v))
-        big = max(g for g, _ in copy)
-        return kern, [v for g, v in copy if g == big]
+                copy.append(v)
+        # the calibration copy moves more bytes than any other copy of the run
+        return kern, max(copy)
 
     fk, fc = per_kernel(_pmc_rows(fetch_dir), "FETCH_SIZE")
     wk, wc = per_kernel(_pmc_rows(write_dir), "WRITE_SIZE")
-    f_scale = med(fc) / CALIBRATION_BYTES  # counter bytes per byte copied
-    w_scale = med(wc) / CALIBRATION_BYTES
+    f_scale = fc / CALIBRATION_BYTES  # counter bytes per byte copied
+    w_scale = wc / CALIBRATION_BYTES
+    # a call's kernels run once per call; the B preparation runs once per run
+    most = max(len(v) for v in fk.values())
     kernels = {}
     for name in sorted(set(fk) | set(wk)):
+        if len(fk.get(name, [])) < most / 2:
+            continue
         kernels[name] = {"dispatches": [len(fk.get(name, [])), len(wk.get(name, []))],
                          "fetch_bytes": round(med(fk[name]) / f_scale) if name in fk else 0,
                          "write_bytes": round(med(wk[name]) / w_scale) if name in wk else 0}
@@ -457,6 +461,26 @@ def summarize_pmc(fetch_dir, write_dir, command):
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+
+
+def kernel_signature(w):
+    """The GEMM kernel instantiation the library runs for a workload, as the
+    profiler names it (without namespace): gemm_kernel<MT, NT, WN, WK, KPW,
+    pre-quantized, staged rows, epilogue> or gemm_wide_kernel<MW, NW, W, D,
+    LDS-staged B>, read off the schedule name."""
+    import re
+    import block_scaled_mxfp4_bf16_amd as mx
+    name = mx.mxfp4_gemm_schedule_name(w.M, w.N, w.K)
+    m = re.match(r"(wide|widel)_mt(\d+)_nt(\d+)_w(\d+)_d(\d+)_split\d+$", name)
+    if m:
+        return "gemm_wide_kernel<%s, %s, %s, %s, %s>" % (m.group(2), m.group(3), m.group(4), m.group(5),
+                                                        "true" if m.group(1) == "widel" else "false")
+    m = re.match(r"mt(\d+)_nt(\d+)_wn(\d+)_wk(\d+)_kpw(\d+)_(split|streamk)\d+(.*)$", name)
+    rest = m.group(7)
+    epi = 2 if m.group(6) == "streamk" else (1 if rest.endswith("_at") else 0)
+    return "gemm_kernel<%s, %s, %s, %s, %s, %s, %d, %d>" % (m.group(1), m.group(2), m.group(3), m.group(4), m.group(5),
+                                                           "true" if "_pq" in rest else "false",
+                                                           8 if "_r8" in rest else 16, epi)
 
 
 def summarize_mfma(pmc_dir, configs, command):
@@ -476,10 +500,17 @@ def summarize_mfma(pmc_dir, configs, command):
         disp = d.setdefault(r["Dispatch_Id"], {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
         disp[r["Counter_Name"]] = float(r["Counter_Value"])
     med = lambda v: sorted(v)[len(v) // 2]
-    want = {}
+    by_sig = {}
     for c in configs:
         w = syn.CONFIGS.get(c) or syn.EXTRA_SHAPES[c]
-        want[expected_mfma(w.M, w.N, w.K)] = w.name
+        by_sig.setdefault(kernel_signature(w), []).append((expected_mfma(w.M, w.N, w.K), w.name))
+
+    def workload_of(kernel, inst):
+        # the instantiation, then the instruction count where workloads share
+        # one (a schedule whose waves x steps overrun K issues more)
+        c = by_sig.get(kernel.replace("void ", "").split("mxfp4::")[-1], [])
+        exact = [n for i, n in c if i == inst]
+        return exact[0] if exact else (c[0][1] if len(c) == 1 else None)
     out = {"command": command, "kernels": []}
     for (name, grid), d in sorted(groups.items()):
         ds = list(d.values())
@@ -487,7 +518,8 @@ def summarize_mfma(pmc_dir, configs, command):
         busy = med([x.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for x in ds])
         ns = med([x["ns"] for x in ds])
         out["kernels"].append({
-            "kernel": name, "grid": grid, "dispatches": len(ds), "workload": want.get(int(inst)),
+            "kernel": name, "grid": grid, "dispatches": len(ds),
+            "workload": workload_of(name, int(inst)),
             "mfma_instructions": int(inst), "busy_simd_cycles": int(busy),
             "busy_cycles_per_instruction": round(busy / inst, 2) if inst else None,
             "duration_ns": ns, "matrix_busy_frac_at_2400MHz": round(busy / (1024 * 2.4 * ns), 4) if ns else None})

@@ -53,7 +53,7 @@ def test_expected_matrix_instructions():
 
 def test_summarize_mfma_on_synthetic_counters(tmp_path, capsys):
     wide = "void mxfp4::gemm_wide_kernel<4, 7, 4, 2, false>(unsigned char const*)"
-    fused = "void mxfp4::gemm_kernel<1, 1, 4, 1, 4, false, 16, 0>(unsigned short const*)"
+    fused = "void mxfp4::gemm_kernel<1, 2, 1, 4, 1, false, 16, 0>(unsigned short const*)"  # c2's schedule
     quant = "mxfp4::quant_quad_kernel(unsigned short const*)"
     rows = []
     for i, ns in enumerate([16000, 16400, 17000]):  # median duration 16400
@@ -86,6 +86,11 @@ def test_summarize_pmc_scales_by_the_copy_calibration(tmp_path, monkeypatch, cap
     # FETCH_SIZE reads half of a cold copy's bytes, WRITE_SIZE all of them (KiB per dispatch)
     fetch = [(1, 1 << 20, copy, "FETCH_SIZE", 64, 0, 1), (2, 1 << 26, copy, "FETCH_SIZE", cal / 2 / 1024, 0, 1)]
     write = [(1, 1 << 20, copy, "WRITE_SIZE", 64, 0, 1), (2, 1 << 26, copy, "WRITE_SIZE", cal / 1024, 0, 1)]
+    prep = "mxfp4::quantize_raw_kernel<false>(unsigned short const*)"  # once per run: not part of a call
+    fetch.append((3, 1 << 20, prep, "FETCH_SIZE", 99999, 0, 1))
+    write.append((3, 1 << 20, prep, "WRITE_SIZE", 99999, 0, 1))
+    fetch.append((4, 1 << 30, copy, "FETCH_SIZE", 100, 0, 1))  # a larger grid, fewer bytes than the calibration
+    write.append((4, 1 << 30, copy, "WRITE_SIZE", 100, 0, 1))
     for i, (f, w) in enumerate([(700, 256), (720, 256), (760, 256)]):
         fetch.append((10 + 2 * i, 65536, gemm, "FETCH_SIZE", f, 0, 1))
         write.append((10 + 2 * i, 65536, gemm, "WRITE_SIZE", w, 0, 1))
@@ -99,6 +104,7 @@ def test_summarize_pmc_scales_by_the_copy_calibration(tmp_path, monkeypatch, cap
     k = out["kernels"]["void mxfp4::gemm_wide_kernel<4, 7, 4, 2, false>"]
     assert k["fetch_bytes"] == 720 * 1024 * 2  # median, divided by the fetch scale
     assert k["write_bytes"] == 256 * 1024 and k["dispatches"] == [3, 3]
+    assert set(out["kernels"]) == {"void mxfp4::gemm_wide_kernel<4, 7, 4, 2, false>", "mxfp4::quant_quad_kernel"}
     assert out["fetch_bytes_per_call"] == 720 * 2048 + 100 * 2048
     assert out["write_bytes_per_call"] == 256 * 1024 + 30 * 1024
     assert out["hbm_bytes_per_call"] == out["fetch_bytes_per_call"] + out["write_bytes_per_call"]
