@@ -231,9 +231,14 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
     uint32_t sb[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
+      // subtile nt's 32-row scale block is (gw + nt) / 2: dword nt / 2 of
+      // those loaded, or (nt + 1) / 2 when gw is odd (only with NT odd: for
+      // NT even every wave's gw is even); a select of two registers, not an
+      // indexed one
       const int g = gw + nt;
       const uint32_t sel = (uint32_t)((g & 1) | ((ks & 1) << 1));
-      sb[nt] = (sword[i][nt >> 1] >> (8 * sel)) & 0xFFu;
+      const uint32_t dw = (NT % 2 == 0) ? sword[i][nt >> 1] : ((gw & 1) ? sword[i][(nt + 1) >> 1] : sword[i][nt >> 1]);
+      sb[nt] = (dw >> (8 * sel)) & 0xFFu;
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {

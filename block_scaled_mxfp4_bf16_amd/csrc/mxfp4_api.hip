@@ -84,7 +84,7 @@ const Tuned kTuned[] = {
     {4, 2880, 512, "mt1_nt2_wn1_wk4_kpw1_split1"},
     {16, 2112, 7168, "mt1_nt1_wn4_wk4_kpw4_split4"},
     {32, 2880, 512, "mt1_nt1_wn4_wk1_kpw4_split1"},
-    {256, 3072, 1536, "mt1_nt2_wn8_wk2_kpw8_split1"},
+    {256, 3072, 1536, "mt2_nt2_wn3_wk4_kpw3_split1"},
 };
 
 // Estimated cost of a large-M schedule, in log-microseconds on the same
@@ -172,6 +172,9 @@ bool pick_schedule(int M, int N, int K, Schedule *out, bool need_pq = false) {
     Schedule s;
     gemm_variant_shape(v, &s);
     if (s.mt != mt || s.pq != (need_pq ? 1 : 0) || s.wide || s.epi) continue;  // atomic and stream-K: named only
+    // the estimate was fitted on power-of-two column tiles; the 96- and
+    // 112-column tiles serve the shapes of the table
+    if ((s.nt * s.wn) & (s.nt * s.wn - 1)) continue;
     if (!need_pq && (s.rb == 8) != (M <= 8)) continue;
     for (s.split = 1; s.split <= 16; ++s.split) {
       if (!covers(s, M, N, K)) continue;

@@ -23,7 +23,7 @@ import torch
 import block_scaled_mxfp4_bf16_amd as mx
 
 
-def prepare(M, N, K, quantized_a, steps, seed=0):
+def prepare(M, N, K, quantized_a, steps, min_bytes=1 << 30, seed=0):
     g = torch.Generator(device="cuda").manual_seed(seed)
     a = torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16)
     b = torch.randn((N, K), generator=g, device="cuda").to(torch.bfloat16)
@@ -37,7 +37,7 @@ def prepare(M, N, K, quantized_a, steps, seed=0):
         a_in = (a,)
         a_bytes = 2 * M * K
     per_set = a_bytes + bw.numel() + bs.numel() + 2 * M * N
-    need = math.ceil((1 << 30) / per_set)
+    need = math.ceil(min_bytes / per_set)
     sets = steps * math.ceil(need / steps)
     bufs = []
     for i in range(sets):
@@ -90,12 +90,15 @@ def time_schedule(M, N, K, quantized_a, bufs, stream, name, steps):
         mx.mxfp4_set_schedule_override(None)
 
 
-def tune(M, N, K, quantized_a=False, steps=50, top=10, confirm=3, log=print):
+def tune(M, N, K, quantized_a=False, steps=50, top=10, confirm=3, log=print, min_bytes=1 << 30):
+    """Time every schedule for (M, N, K); see the module docstring.  The
+    buffer sets total at least `min_bytes` (the default keeps every call's
+    inputs out of the caches; smaller is for quick checks only)."""
     names = mx.mxfp4_list_schedules(M, N, K, quantized_a)
     if not names:
         raise ValueError("no schedule serves %dx%dx%d" % (M, N, K))
     builtin = (mx.mxfp4_gemm_q_schedule_name if quantized_a else mx.mxfp4_gemm_schedule_name)(M, N, K)
-    bufs = prepare(M, N, K, quantized_a, steps)
+    bufs = prepare(M, N, K, quantized_a, steps, min_bytes)
     stream = torch.cuda.Stream()
     times = {}
     for i, n in enumerate(names):

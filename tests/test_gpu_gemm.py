@@ -483,7 +483,7 @@ def test_tuner_times_every_listed_schedule():
     the finalists include the built-in choice, and the best one is listed."""
     torch_cuda()
     from block_scaled_mxfp4_bf16_amd import tune
-    res = tune.tune(16, 256, 512, steps=10, top=2, confirm=1, log=lambda s: None)
+    res = tune.tune(16, 256, 512, steps=10, top=2, confirm=1, log=lambda s: None, min_bytes=4 << 20)
     names = mx.mxfp4_list_schedules(16, 256, 512)
     assert set(res["times_us"]) == set(names)
     assert all(t > 0 for t in res["times_us"].values())
@@ -512,7 +512,34 @@ def test_tuner_with_quantized_a():
     finalists."""
     torch_cuda()
     from block_scaled_mxfp4_bf16_amd import tune
-    res = tune.tune(32, 256, 1024, quantized_a=True, steps=10, top=1, confirm=1, log=lambda s: None)
+    res = tune.tune(32, 256, 1024, quantized_a=True, steps=10, top=1, confirm=1, log=lambda s: None,
+                    min_bytes=4 << 20)
     assert set(res["times_us"]) == set(mx.mxfp4_list_schedules(32, 256, 1024, True))
     assert res["builtin"] == mx.mxfp4_gemm_q_schedule_name(32, 256, 1024)
     assert res["builtin"] in res["confirmed_us"]
+
+
+# Tiles with an odd number of 16-column subtiles per wave (every other tile
+# starts on an odd column group, whose B scales sit in the upper half of a
+# scale dword) and 32 x 96 tiles; split K, rows past M and a final half step.
+ODD_TILE_CASES = [("mt1_nt7_wn1_wk4_kpw4_split1", 64, 7168, 2048), ("mt1_nt7_wn1_wk8_kpw2_split2", 20, 448, 2112),
+                  ("mt1_nt7_wn1_wk16_kpw1_split1", 5, 224, 1024), ("mt1_nt7_wn1_wk2_kpw8_split3", 17, 448, 4160),
+                  ("mt2_nt6_wn1_wk4_kpw3_split1", 256, 3072, 1536), ("mt2_nt3_wn2_wk4_kpw3_split2", 40, 288, 1600),
+                  ("mt2_nt6_wn1_wk6_kpw2_split1", 33, 192, 1536), ("mt2_nt3_wn2_wk2_kpw6_split1", 70, 96, 1536),
+                  ("mt2_nt2_wn3_wk4_kpw3_split1", 256, 3072, 1536), ("mt2_nt1_wn6_wk2_kpw6_split1", 40, 192, 1536),
+                  ("mt1_nt1_wn7_wk2_kpw8_split2", 9, 224, 4096), ("mt2_nt2_wn3_wk3_kpw4_split2", 31, 96, 2112)]
+
+
+@pytest.mark.parametrize("sched,M,N,K", ODD_TILE_CASES)
+def test_odd_and_wide_tiles_match_oracle(sched, M, N, K):
+    torch = torch_cuda()
+    c = make(torch, M, N, K, seed=M + N + K + 9)
+    mx.mxfp4_set_schedule_override(sched)
+    try:
+        assert mx.mxfp4_gemm_schedule_name(M, N, K) == sched
+        first = c.run()
+        second = c.run()
+    finally:
+        mx.mxfp4_set_schedule_override(None)
+    assert np.array_equal(first, second)
+    assert_close(first, c.ref(), "%s %dx%dx%d" % (sched, M, N, K))
