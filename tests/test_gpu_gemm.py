@@ -95,16 +95,11 @@ def test_config_c5_full_match():
 
 @pytest.mark.parametrize("name", list(syn.EXTRA_SHAPES))
 def test_leaderboard_shapes(name):
+    """The other leaderboard shapes on the pages, every output compared."""
     torch = torch_cuda()
     w = syn.EXTRA_SHAPES[name]
     c = Case(torch, w.a_bits(), w.b_bits())
-    got = c.run()
-    if w.M * w.N * w.K <= 3e8:
-        assert_close(got, c.ref(), name)
-    else:
-        rng = np.random.default_rng(1)
-        ms, ns = rng.integers(0, w.M, 3000), rng.integers(0, w.N, 3000)
-        assert_close(got[ms, ns], c.ref_sampled(ms, ns), name)
+    assert_close(c.run(), c.ref(), name)
 
 
 # A spread over the compiled kernels: one and many waves along N and K,
