@@ -466,8 +466,8 @@ def summarize_pmc(fetch_dir, write_dir, command):
 def kernel_signature(w):
     """The GEMM kernel instantiation the library runs for a workload, as the
     profiler names it (without namespace): gemm_kernel<MT, NT, WN, WK, KPW,
-    pre-quantized, staged rows, epilogue> or gemm_wide_kernel<MW, NW, W, D,
-    LDS-staged B>, read off the schedule name."""
+    pre-quantized, staged rows, epilogue, phase stamps (always off)> or
+    gemm_wide_kernel<MW, NW, W, D, LDS-staged B>, read off the schedule name."""
     import re
     import block_scaled_mxfp4_bf16_amd as mx
     name = mx.mxfp4_gemm_schedule_name(w.M, w.N, w.K)
@@ -478,7 +478,7 @@ def kernel_signature(w):
     m = re.match(r"mt(\d+)_nt(\d+)_wn(\d+)_wk(\d+)_kpw(\d+)_(split|streamk)\d+(.*)$", name)
     rest = m.group(7)
     epi = 2 if m.group(6) == "streamk" else (1 if rest.endswith("_at") else 0)
-    return "gemm_kernel<%s, %s, %s, %s, %s, %s, %d, %d>" % (m.group(1), m.group(2), m.group(3), m.group(4), m.group(5),
+    return "gemm_kernel<%s, %s, %s, %s, %s, %s, %d, %d, false>" % (m.group(1), m.group(2), m.group(3), m.group(4), m.group(5),
                                                            "true" if "_pq" in rest else "false",
                                                            8 if "_r8" in rest else 16, epi)
 
@@ -617,6 +617,115 @@ def floors(torch, steps, samples, names):
     return out
 
 
+# The split-1 schedules the phase probe instantiates with stamps, by probe
+# index: (workload, schedule name the library must pick for it).
+PHASE_PROBES = {"c2": (0, "mt1_nt2_wn1_wk4_kpw1_split1"), "c3": (1, "mt1_nt1_wn1_wk14_kpw4_split1_r8")}
+PHASE_NAMES = ["loads_issued", "a_staged", "products_done", "c_stores_issued", "c_stores_complete"]
+
+
+def phases(torch, mx, steps, names=("c2", "c3")):
+    """Where the time of one small-M call goes: the probe library's copy of
+    the fused kernel (the library's code, built with its flags, plus six
+    100 MHz real-time stamps per wave) runs the workload under the cold
+    rotation of the GEMM timing, in graphs of `steps` calls.  Per wave the
+    phases are entry -> loads issued -> A staged (A has arrived, been
+    quantized and written to LDS) -> products done (B has arrived and the
+    matrix instructions issued; with several K waves, the partial sums are in
+    LDS) -> C stores issued -> C stores complete.  Reported: the medians and
+    90th percentiles of each phase over all waves of the last graph's calls;
+    the spread of wave entry times within a call (how long the launch takes
+    to start every workgroup); the span from the first entry to the last
+    completion; and the stamped calls' time per call from the graph replay,
+    beside the library's own.  The stamped C is checked bit for bit against
+    the library's."""
+    import ctypes
+    L = ctypes.CDLL(PROBES_LIB)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    L.mxfp4_probe_phases.argtypes = [I, P, P, P, P, P, ctypes.c_size_t, I, I, I, I, P]
+    L.mxfp4_probe_phases_waves.argtypes = [I]
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+    out = {}
+    for name in names:
+        which, sched = PHASE_PROBES[name]
+        w = workload(name)
+        M, N, K = w.M, w.N, w.K
+        if mx.mxfp4_gemm_schedule_name(M, N, K) != sched:
+            out[name] = {"skipped": "the library picks %s" % mx.mxfp4_gemm_schedule_name(M, N, K)}
+            continue
+        waves = L.mxfp4_probe_phases_waves(which)
+        nt = 2 if which == 0 else 1  # both schedules have one 16-row m tile and one column wave
+        grid = (N // (16 * nt)) * ((M + 15) // 16)
+        words = grid * waves * 8
+        sets, graphs = rotation(set_bytes(M, N, K), steps)
+        bufs = prepare(torch, mx, w, sets)
+        stamps = [torch.zeros(words, dtype=torch.int64, device="cuda") for _ in range(steps)]
+        ref = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+        def call(i):
+            A, Bw, Bs, C = bufs[i % sets]
+            rc = L.mxfp4_probe_phases(which, A.data_ptr(), Bw.data_ptr(), Bs.data_ptr(), C.data_ptr(),
+                                      stamps[i % steps].data_ptr(), words, M, N, K, 0, sh)
+            if rc != 0:
+                raise RuntimeError("phase probe %s: error %d" % (name, rc))
+
+        with torch.cuda.stream(stream):
+            mx.mxfp4_reserve(M, N, K, stream=stream)
+            mx.mxfp4_gemm(bufs[0][0], bufs[0][1], bufs[0][2], ref, M, N, K, stream=stream)
+            call(0)
+        stream.synchronize()
+        same = bool(torch.equal(ref.view(torch.int16), bufs[0][3].view(torch.int16)))
+
+        def graph_us(fn):
+            gs = []
+            for j in range(graphs):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for i in range(steps):
+                        fn(j * steps + i)
+                gs.append(g)
+            with torch.cuda.stream(stream):
+                for g in gs:
+                    g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                for g in gs:
+                    g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / (graphs * steps)
+
+        lib_us = graph_us(lambda i: mx.mxfp4_gemm(bufs[i % sets][0], bufs[i % sets][1], bufs[i % sets][2],
+                                                  bufs[i % sets][3], M, N, K, stream=stream))
+        stamped_us = graph_us(call)
+        per_phase = [[] for _ in PHASE_NAMES]
+        spread, span = [], []
+        for st in stamps:
+            t = st.view(grid * waves, 8)[:, :6].cpu().tolist()
+            for r in t:
+                for k in range(5):
+                    per_phase[k].append((r[k + 1] - r[k]) * 0.01)
+            spread.append((max(r[0] for r in t) - min(r[0] for r in t)) * 0.01)
+            span.append((max(r[5] for r in t) - min(r[0] for r in t)) * 0.01)
+        out[name] = {
+            "schedule": sched, "workgroups": grid, "waves_per_workgroup": waves,
+            "library_us_per_call": round(lib_us, 3), "stamped_us_per_call": round(stamped_us, 3),
+            "c_matches_library": same,
+            "wave_phase_us": {n: {"median": round(percentile(v, 50), 3), "p90": round(percentile(v, 90), 3),
+                                  "min": round(min(v), 3), "max": round(max(v), 3)}
+                              for n, v in zip(PHASE_NAMES, per_phase)},
+            "entry_spread_us": {"median": round(percentile(spread, 50), 3), "p90": round(percentile(spread, 90), 3)},
+            "first_entry_to_last_completion_us": {"median": round(percentile(span, 50), 3),
+                                                  "p90": round(percentile(span, 90), 3)},
+        }
+        print("[phases] %s: %s" % (name, json.dumps(out[name])), file=sys.stderr, flush=True)
+        del bufs, stamps
+        torch.cuda.empty_cache()
+    return out
+
+
 def workload(name):
     import synthetic as syn
     return syn.CONFIGS.get(name) or syn.EXTRA_SHAPES[name]
@@ -643,7 +752,8 @@ def main():
     ap.add_argument("--no-clocks", action="store_true", help="skip reading the GPU clocks with amd-smi")
     ap.add_argument("--floors", action="store_true",
                     help="measure the machine's floors with the probe library instead (launch, B streaming, "
-                         "matrix-instruction rate and clock) and print them as one JSON line")
+                         "matrix-instruction rate and clock, and the per-phase timing of the small-M kernel for "
+                         "c2 and c3 when listed) and print them as one JSON line")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="first run a cold 256 MiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -665,8 +775,10 @@ def main():
     torch.cuda.set_device(0)
     if args.floors:
         names = [c for c in args.configs.split(",") if c]
-        print(json.dumps({"floors": floors(torch, args.steps, args.samples, names), "steps": args.steps,
-                          "samples": args.samples, "clocks": clocks_before}), flush=True)
+        fl = floors(torch, args.steps, args.samples, names)
+        fl["phases"] = phases(torch, mx, args.steps, [n for n in names if n in PHASE_PROBES])
+        print(json.dumps({"floors": fl, "steps": args.steps, "samples": args.samples, "clocks": clocks_before}),
+              flush=True)
         return
     if args.pmc_calibration:
         calibration_copy(torch)

@@ -10,8 +10,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmxfp4.so")
 # Measurement probes for bench.py --floors (a library of their own: nothing
-# in libmxfp4.so uses them).
-PROBES_SRC = "probes.hip"
+# in libmxfp4.so uses them).  probe_phases.hip instantiates the fused kernel
+# and so takes the library's flags; probes.hip has its own.
+PROBES_SOURCES = ["probes.hip", "probe_phases.hip"]
 PROBES_LIB = os.path.join(PKG, "libmxfp4_probes.so")
 SOURCES = ["mxfp4_api.hip", "quant_kernels.hip", "gemm_kernels.hip", "gemm_wide.hip"] + [
     "gemm_table_%d.hip" % i for i in range(8)]
@@ -69,16 +70,22 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             sys.stderr.write(text)
         elif verbose and lines:
             sys.stderr.write("\n".join(lines) + "\n")
-    probe_cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS[PROBES_SRC], "-shared", "-o", PROBES_LIB + ".tmp%d" % os.getpid(),
-                 os.path.join(CSRC, PROBES_SRC)]
-    pp = subprocess.run(probe_cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
-    if pp.returncode != 0:
-        failed.append(PROBES_SRC)
-        sys.stderr.write(pp.stdout.decode(errors="replace"))
-    else:
-        os.replace(PROBES_LIB + ".tmp%d" % os.getpid(), PROBES_LIB)
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
+    probe_objs = [os.path.join(objdir, "probe_" + src.replace(".hip", ".o")) for src in PROBES_SOURCES]
+    pprocs = [(src, subprocess.Popen([hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+                                      "-o", obj], stdout=subprocess.PIPE, stderr=subprocess.STDOUT))
+              for src, obj in zip(PROBES_SOURCES, probe_objs)]
+    for src, p in pprocs:
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            failed.append(src)
+            sys.stderr.write(out.decode(errors="replace"))
+    if failed:
+        raise RuntimeError("hipcc failed for: " + ", ".join(failed))
+    ptmp = PROBES_LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", ptmp, *probe_objs])
+    os.replace(ptmp, PROBES_LIB)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

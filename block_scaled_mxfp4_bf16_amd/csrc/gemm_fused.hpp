@@ -61,7 +61,13 @@
 namespace mxfp4 {
 
 // `split`: workgroups per tile (EPI 0, 1) or of the whole grid (EPI 2).
-template <int MT, int NT, int WN, int WK, int KPW, bool PREQ, int RB, int EPI>
+// STAMPS (measurement probes only; every schedule of the library has it
+// off): each wave records the 100 MHz real-time counter at the kernel's
+// phase boundaries -- entry, loads issued, A staged, products reduced, C
+// stores issued, C stores completed -- in scalar registers, and lane 0
+// writes the six stamps at the end to `partials`, read as uint64
+// [workgroups * waves][8].  Split-1 schedules only.
+template <int MT, int NT, int WN, int WK, int KPW, bool PREQ, int RB, int EPI, bool STAMPS = false>
 __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__restrict__ A,
                                                            const uint8_t *__restrict__ Aop,
                                                            const uint8_t *__restrict__ Bw,
@@ -113,6 +119,23 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
   // One segment: steps [S0, S1) of tile (m_tile, n_tile), whose K range is
   // shared by `nparts` workgroups; slot(j) is the partial tile of the j-th
   // of them and this workgroup is number `mine_j`.
+  uint64_t stamp[6];
+  auto take = [&](int i) {
+    if constexpr (STAMPS) stamp[i] = __builtin_amdgcn_s_memrealtime();
+  };
+  auto write_stamps = [&]() {
+    if constexpr (STAMPS) {
+      static_assert(EPI == 0, "stamps serve split-1 schedules");
+      __builtin_amdgcn_s_waitcnt(0);
+      take(5);
+      if (lane == 0) {
+        uint64_t *out = (uint64_t *)partials + ((size_t)blockIdx.x * WAVES + wave) * 8;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) out[i] = stamp[i];
+      }
+    }
+  };
+  take(0);
   auto segment = [&](const int m_tile, const int n_tile, const int S0, const int S1, const int nparts,
                      const int mine_j, auto slot) {
   const int m0 = m_tile * 16 * MT;
@@ -178,6 +201,8 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
     }
   }
 
+  take(1);
+
   // Phase 2: quantize the staged A blocks into LDS (the encoder is chosen
   // once for all blocks, so the hardware path is straight-line code).
   if constexpr (!PREQ) {
@@ -217,6 +242,8 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
       __syncthreads();
     }
   }
+
+  take(2);
 
   // Phase 3: accumulate.
   v4f acc[MT][NT];
@@ -286,12 +313,23 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
 
   if constexpr (WK == 1) {
     if (nparts == 1) {
+      if constexpr (STAMPS) {
+        // the stamp follows the last product: an empty statement that reads
+        // every accumulator keeps the compiler from moving it earlier
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) asm volatile("" ::"v"(acc[mt][nt]));
+      }
+      take(3);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) store_c(elem(mt, nt, r), acc[mt][nt][r]);
+      take(4);
+      write_stamps();
       return;
     }
   } else {
@@ -304,6 +342,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
 #pragma unroll
         for (int r = 0; r < 4; ++r) red[wk * E + elem(mt, nt, r)] = acc[mt][nt][r];
     __syncthreads();
+    take(3);
     if (nparts == 1) {
       // eight consecutive elements are eight consecutive columns of one row:
       // add them over the WK waves and store them as one 16-byte write
@@ -333,6 +372,8 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
           *(u32x4 *)(C + (size_t)row * N + col) = pk;
         }
       }
+      take(4);
+      write_stamps();
       return;
     }
   }

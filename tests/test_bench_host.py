@@ -53,7 +53,7 @@ def test_expected_matrix_instructions():
 
 def test_summarize_mfma_on_synthetic_counters(tmp_path, capsys):
     wide = "void mxfp4::gemm_wide_kernel<4, 7, 4, 2, false>(unsigned char const*)"
-    fused = "void mxfp4::gemm_kernel<1, 2, 1, 4, 1, false, 16, 0>(unsigned short const*)"  # c2's schedule
+    fused = "void mxfp4::gemm_kernel<1, 2, 1, 4, 1, false, 16, 0, false>(unsigned short const*)"  # c2's schedule
     quant = "mxfp4::quant_quad_kernel(unsigned short const*)"
     rows = []
     for i, ns in enumerate([16000, 16400, 17000]):  # median duration 16400

@@ -21,3 +21,18 @@ def test_floor_probes_run_and_are_plausible():
         assert 0 < m["tflops"] <= bench.FP4_PEAK_TFLOPS * 1.05
         assert 1000 < m["shader_mhz"] < 3000
         assert m["cycles_per_instruction_per_wave"] >= 15.5
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_phase_probe_matches_library_and_stamps_are_ordered(name):
+    """The stamped copy of the fused kernel writes the library's C bit for
+    bit, and every wave's stamps come in phase order."""
+    torch = torch_cuda()
+    import block_scaled_mxfp4_bf16_amd as mx
+    out = bench.phases(torch, mx, steps=2, names=[name])[name]
+    assert "skipped" not in out, out
+    assert out["c_matches_library"]
+    for ph in bench.PHASE_NAMES:
+        assert out["wave_phase_us"][ph]["min"] >= 0.0
+    assert 0.0 < out["first_entry_to_last_completion_us"]["median"] < 1000.0
+    assert out["entry_spread_us"]["median"] <= out["first_entry_to_last_completion_us"]["median"]
