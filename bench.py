@@ -467,14 +467,15 @@ def kernel_signature(w):
     """The GEMM kernel instantiation the library runs for a workload, as the
     profiler names it (without namespace): gemm_kernel<MT, NT, WN, WK, KPW,
     pre-quantized, staged rows, epilogue, phase stamps (always off)> or
-    gemm_wide_kernel<MW, NW, W, D, LDS-staged B>, read off the schedule name."""
+    gemm_wide_kernel<MW, NW, W, D, LDS-staged B, phase stamps (always off)>,
+    read off the schedule name."""
     import re
     import block_scaled_mxfp4_bf16_amd as mx
     name = mx.mxfp4_gemm_schedule_name(w.M, w.N, w.K)
     m = re.match(r"(wide|widel)_mt(\d+)_nt(\d+)_w(\d+)_d(\d+)_split\d+$", name)
     if m:
-        return "gemm_wide_kernel<%s, %s, %s, %s, %s>" % (m.group(2), m.group(3), m.group(4), m.group(5),
-                                                        "true" if m.group(1) == "widel" else "false")
+        return "gemm_wide_kernel<%s, %s, %s, %s, %s, false>" % (m.group(2), m.group(3), m.group(4), m.group(5),
+                                                               "true" if m.group(1) == "widel" else "false")
     m = re.match(r"mt(\d+)_nt(\d+)_wn(\d+)_wk(\d+)_kpw(\d+)_(split|streamk)\d+(.*)$", name)
     rest = m.group(7)
     epi = 2 if m.group(6) == "streamk" else (1 if rest.endswith("_at") else 0)
@@ -726,6 +727,116 @@ def phases(torch, mx, steps, names=("c2", "c3")):
     return out
 
 
+WIDE_PHASE_SCHEDULE = "wide_mt4_nt7_w4_d2_split1"
+WIDE_PHASE_NAMES = ["k_loop", "partials_in_lds", "sums_and_c_stores_issued", "c_stores_complete"]
+
+
+def wide_phases(torch, mx, steps, name="c5"):
+    """Where the time of a large-M call goes: the probe library runs the
+    library's A quantization and its 64 x 112-tile K loop with five 100 MHz
+    real-time stamps per wave (entry, K loop done, partial tiles in LDS, C
+    stores issued, complete), two launches per call as the library does,
+    under the cold rotation of the GEMM timing.  Reported per workgroup
+    (medians and 90th percentiles over the last graph's calls): the K loop
+    from the first wave's entry to the last wave's last product, the
+    partial tiles' trip into LDS, the summing and C stores, and their
+    completion; per call: the spread of workgroup entries and of K-loop
+    ends, and the span from the first entry to the last completion; per
+    XCD: the median completion time.  The stamped C is checked bit for bit
+    against the library's."""
+    import ctypes
+    L = ctypes.CDLL(PROBES_LIB)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    L.mxfp4_probe_wide_operand_bytes.argtypes = [I, I]
+    L.mxfp4_probe_wide_operand_bytes.restype = ctypes.c_size_t
+    L.mxfp4_probe_wide_quant.argtypes = [P, P, I, I, P]
+    L.mxfp4_probe_wide_phases.argtypes = [P, P, P, P, P, ctypes.c_size_t, I, I, I, P]
+    w = workload(name)
+    M, N, K = w.M, w.N, w.K
+    if mx.mxfp4_gemm_schedule_name(M, N, K) != WIDE_PHASE_SCHEDULE:
+        return {"skipped": "the library picks %s" % mx.mxfp4_gemm_schedule_name(M, N, K)}
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+    G = (N // 112) * ((M + 63) // 64)
+    words = G * 4 * 8
+    sets, graphs = rotation(set_bytes(M, N, K), steps)
+    bufs = prepare(torch, mx, w, sets)
+    aop = torch.zeros(L.mxfp4_probe_wide_operand_bytes(M, K), dtype=torch.uint8, device="cuda")
+    stamps = [torch.zeros(words, dtype=torch.int64, device="cuda") for _ in range(steps)]
+    ref = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def call(i):
+        A, Bw, Bs, C = bufs[i % sets]
+        rc = L.mxfp4_probe_wide_quant(A.data_ptr(), aop.data_ptr(), M, K, sh)
+        rc = rc or L.mxfp4_probe_wide_phases(aop.data_ptr(), Bw.data_ptr(), Bs.data_ptr(), C.data_ptr(),
+                                             stamps[i % steps].data_ptr(), words, M, N, K, sh)
+        if rc != 0:
+            raise RuntimeError("wide phase probe: error %d" % rc)
+
+    with torch.cuda.stream(stream):
+        mx.mxfp4_reserve(M, N, K, stream=stream)
+        mx.mxfp4_gemm(bufs[0][0], bufs[0][1], bufs[0][2], ref, M, N, K, stream=stream)
+        call(0)
+    stream.synchronize()
+    same = bool(torch.equal(ref.view(torch.int16), bufs[0][3].view(torch.int16)))
+
+    def graph_us(fn):
+        gs = []
+        for j in range(graphs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(steps):
+                    fn(j * steps + i)
+            gs.append(g)
+        with torch.cuda.stream(stream):
+            for g in gs:
+                g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for g in gs:
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (graphs * steps)
+
+    lib_us = graph_us(lambda i: mx.mxfp4_gemm(bufs[i % sets][0], bufs[i % sets][1], bufs[i % sets][2],
+                                              bufs[i % sets][3], M, N, K, stream=stream))
+    stamped_us = graph_us(call)
+    per_wg = {n: [] for n in WIDE_PHASE_NAMES}
+    entry_spread, loop_end_spread, span = [], [], []
+    xcd_end = {}
+    for st in stamps:
+        t = st.view(G, 4, 8)[:, :, :6].cpu().tolist()
+        T0 = min(min(wv[0] for wv in wg) for wg in t)
+        ends = []
+        for wg in t:
+            ent = min(wv[0] for wv in wg)
+            le = max(wv[1] for wv in wg)
+            per_wg["k_loop"].append((le - ent) * 0.01)
+            per_wg["partials_in_lds"].append((max(wv[2] for wv in wg) - le) * 0.01)
+            per_wg["sums_and_c_stores_issued"].append(percentile([wv[3] - wv[2] for wv in wg], 50) * 0.01)
+            per_wg["c_stores_complete"].append(percentile([wv[4] - wv[3] for wv in wg], 50) * 0.01)
+            ends.append(le)
+            xcd_end.setdefault(int(wg[0][5]), []).append((max(wv[4] for wv in wg) - T0) * 0.01)
+        entry_spread.append((max(min(wv[0] for wv in wg) for wg in t) - T0) * 0.01)
+        loop_end_spread.append((max(ends) - min(ends)) * 0.01)
+        span.append((max(max(wv[4] for wv in wg) for wg in t) - T0) * 0.01)
+    q = lambda v: {"median": round(percentile(v, 50), 3), "p90": round(percentile(v, 90), 3)}
+    out = {"workload": w.name, "schedule": WIDE_PHASE_SCHEDULE, "workgroups": G, "waves_per_workgroup": 4,
+           "library_us_per_call": round(lib_us, 3), "stamped_us_per_call": round(stamped_us, 3),
+           "c_matches_library": same,
+           "workgroup_phase_us": {n: q(v) for n, v in per_wg.items()},
+           "entry_spread_us": q(entry_spread), "k_loop_end_spread_us": q(loop_end_spread),
+           "first_entry_to_last_completion_us": q(span),
+           "median_completion_by_xcd_us": {str(x): round(percentile(v, 50), 3) for x, v in sorted(xcd_end.items())}}
+    print("[phases] %s: %s" % (name, json.dumps(out)), file=sys.stderr, flush=True)
+    del bufs, stamps
+    torch.cuda.empty_cache()
+    return out
+
+
 def workload(name):
     import synthetic as syn
     return syn.CONFIGS.get(name) or syn.EXTRA_SHAPES[name]
@@ -753,7 +864,7 @@ def main():
     ap.add_argument("--floors", action="store_true",
                     help="measure the machine's floors with the probe library instead (launch, B streaming, "
                          "matrix-instruction rate and clock, and the per-phase timing of the small-M kernel for "
-                         "c2 and c3 when listed) and print them as one JSON line")
+                         "c2 and c3 and of the large-M kernel for c5 when listed) and print them as one JSON line")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="first run a cold 256 MiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -777,6 +888,8 @@ def main():
         names = [c for c in args.configs.split(",") if c]
         fl = floors(torch, args.steps, args.samples, names)
         fl["phases"] = phases(torch, mx, args.steps, [n for n in names if n in PHASE_PROBES])
+        if "c5" in names:
+            fl["phases"]["c5"] = wide_phases(torch, mx, args.steps)
         print(json.dumps({"floors": fl, "steps": args.steps, "samples": args.samples, "clocks": clocks_before}),
               flush=True)
         return

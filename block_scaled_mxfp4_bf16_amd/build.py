@@ -10,9 +10,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmxfp4.so")
 # Measurement probes for bench.py --floors (a library of their own: nothing
-# in libmxfp4.so uses them).  probe_phases.hip instantiates the fused kernel
-# and so takes the library's flags; probes.hip has its own.
-PROBES_SOURCES = ["probes.hip", "probe_phases.hip"]
+# in libmxfp4.so uses them).  probe_phases.hip and probe_wide.hip
+# instantiate the library's kernels and take the flags of the library
+# sources that do; probes.hip has its own.
+PROBES_SOURCES = ["probes.hip", "probe_phases.hip", "probe_wide.hip"]
 PROBES_LIB = os.path.join(PKG, "libmxfp4_probes.so")
 SOURCES = ["mxfp4_api.hip", "quant_kernels.hip", "gemm_kernels.hip", "gemm_wide.hip"] + [
     "gemm_table_%d.hip" % i for i in range(8)]
@@ -36,7 +37,8 @@ HIPCC_FLAGS = [
 # result is tied to its accumulator input when the accumulator lives in
 # AGPRs, so long accumulation loops get copies between every pair of
 # instructions; keeping accumulators in VGPRs lets them update in place.
-EXTRA_FLAGS = {"gemm_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "probes.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA_FLAGS = {"gemm_wide.hip": VGPR_FORM, "probes.hip": VGPR_FORM, "probe_wide.hip": VGPR_FORM}
 
 
 def hipcc() -> str:

@@ -12,6 +12,7 @@ namespace mxfp4 {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -119,6 +120,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Two floats -> packed bf16 (a in the low half), rounded to nearest even by
+// the hardware convert (v_cvt_pk_bf16_f32).  For every finite input it
+// gives the bits of f32_to_bf16_rne; NaN inputs (outside the GEMM's
+// contract) keep a NaN of the hardware's choosing.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, bf16x2));
 }
 
 // Byte offset of (row, group) in a shuffled scale buffer whose rows of 32

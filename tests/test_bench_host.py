@@ -52,7 +52,7 @@ def test_expected_matrix_instructions():
 
 
 def test_summarize_mfma_on_synthetic_counters(tmp_path, capsys):
-    wide = "void mxfp4::gemm_wide_kernel<4, 7, 4, 2, false>(unsigned char const*)"
+    wide = "void mxfp4::gemm_wide_kernel<4, 7, 4, 2, false, false>(unsigned char const*)"
     fused = "void mxfp4::gemm_kernel<1, 2, 1, 4, 1, false, 16, 0, false>(unsigned short const*)"  # c2's schedule
     quant = "mxfp4::quant_quad_kernel(unsigned short const*)"
     rows = []
@@ -79,7 +79,7 @@ def test_summarize_mfma_on_synthetic_counters(tmp_path, capsys):
 
 def test_summarize_pmc_scales_by_the_copy_calibration(tmp_path, monkeypatch, capsys):
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
-    gemm = "void mxfp4::gemm_wide_kernel<4, 7, 4, 2, false>(unsigned char const*)"
+    gemm = "void mxfp4::gemm_wide_kernel<4, 7, 4, 2, false, false>(unsigned char const*)"
     quant = "mxfp4::quant_quad_kernel(unsigned short const*)"
     copy = "__amd_rocclr_copyBuffer"
     cal = bench.CALIBRATION_BYTES
@@ -101,10 +101,10 @@ def test_summarize_pmc_scales_by_the_copy_calibration(tmp_path, monkeypatch, cap
     bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), "cmd")
     out = json.loads(capsys.readouterr().out)
     assert out["copy_calibration"] == {"fetch": 0.5, "write": 1.0}
-    k = out["kernels"]["void mxfp4::gemm_wide_kernel<4, 7, 4, 2, false>"]
+    k = out["kernels"]["void mxfp4::gemm_wide_kernel<4, 7, 4, 2, false, false>"]
     assert k["fetch_bytes"] == 720 * 1024 * 2  # median, divided by the fetch scale
     assert k["write_bytes"] == 256 * 1024 and k["dispatches"] == [3, 3]
-    assert set(out["kernels"]) == {"void mxfp4::gemm_wide_kernel<4, 7, 4, 2, false>", "mxfp4::quant_quad_kernel"}
+    assert set(out["kernels"]) == {"void mxfp4::gemm_wide_kernel<4, 7, 4, 2, false, false>", "mxfp4::quant_quad_kernel"}
     assert out["fetch_bytes_per_call"] == 720 * 2048 + 100 * 2048
     assert out["write_bytes_per_call"] == 256 * 1024 + 30 * 1024
     assert out["hbm_bytes_per_call"] == out["fetch_bytes_per_call"] + out["write_bytes_per_call"]

@@ -36,3 +36,18 @@ def test_phase_probe_matches_library_and_stamps_are_ordered(name):
         assert out["wave_phase_us"][ph]["min"] >= 0.0
     assert 0.0 < out["first_entry_to_last_completion_us"]["median"] < 1000.0
     assert out["entry_spread_us"]["median"] <= out["first_entry_to_last_completion_us"]["median"]
+
+
+def test_wide_phase_probe_matches_library_and_stamps_are_ordered():
+    """The stamped copy of the large-M K loop writes the library's C bit for
+    bit (at 256 x 7168 x 7168, after the same A quantization), and the
+    phases it reports are non-negative."""
+    torch = torch_cuda()
+    import block_scaled_mxfp4_bf16_amd as mx
+    out = bench.wide_phases(torch, mx, steps=2)
+    assert "skipped" not in out, out
+    assert out["c_matches_library"]
+    for ph in bench.WIDE_PHASE_NAMES:
+        assert out["workgroup_phase_us"][ph]["median"] >= 0.0
+    assert 0.0 < out["first_entry_to_last_completion_us"]["median"] < 1000.0
+    assert len(out["median_completion_by_xcd_us"]) >= 1
