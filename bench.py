@@ -135,6 +135,8 @@ def kernel_source_hash():
     h = hashlib.sha256()
     d = os.path.join(ROOT, KERNEL_SOURCE_DIR)
     for rel in sorted(os.listdir(d)):
+        if rel.startswith("probe"):
+            continue  # the measurement probes are not part of the library
         with open(os.path.join(d, rel), "rb") as f:
             h.update(rel.encode())
             h.update(f.read())
