@@ -58,6 +58,18 @@ def alg_bytes(M, N, K):
     return 2 * M * K + N * K // 2 + N * K // 32 + 2 * M * N
 
 
+NOMINAL_SCLK_MHZ = 2400.0       # the clock the published matrix peak assumes
+
+
+def load_sclk_mhz(clocks):
+    """Mean shader clock over the XCDs (amd-smi's gfx_<i> domains) from a
+    reading taken under load, or None."""
+    if not clocks:
+        return None
+    v = [x for k, x in clocks.items() if k.startswith("gfx_") and isinstance(x, (int, float)) and x > 0]
+    return sum(v) / len(v) if v else None
+
+
 def alg_flops(M, N, K):
     return 2 * M * N * K
 
@@ -957,6 +969,13 @@ def main():
     if not args.no_clocks:
         line["clocks"] = {"before": clocks_before, "under_headline_load": h.get("clocks_under_load"),
                           "after": gpu_clocks()}
+        mhz = load_sclk_mhz(h.get("clocks_under_load"))
+        if mhz:
+            # the matrix peak scales with the shader clock: the same fractions
+            # against the peak at the clock measured under load
+            line["clocks"]["sclk_under_load_mhz"] = round(mhz, 1)
+            for r in per.values():
+                r["mfma_frac_at_load_sclk"] = r["mfma_frac"] * NOMINAL_SCLK_MHZ / mhz
     if not args.no_cpu_baseline:
         threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
         line["cpu_baseline"] = cpu_baseline(threads)

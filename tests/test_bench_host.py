@@ -154,3 +154,10 @@ def test_more_than_one_gpu_is_refused():
                        timeout=120)
     assert r.returncode == 1
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_load_sclk_mean_over_xcds():
+    assert bench.load_sclk_mhz(None) is None
+    assert bench.load_sclk_mhz({"mem_0": 2000}) is None
+    c = {"gfx_0": 2400, "gfx_1": 2300, "mem_0": 2000, "socclk_0": 74, "replays": 580}
+    assert bench.load_sclk_mhz(c) == 2350.0
