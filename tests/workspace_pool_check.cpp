@@ -4,19 +4,75 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <atomic>
+#include <map>
+#include <mutex>
+#include <random>
 #include <set>
+#include <thread>
+#include <vector>
 
 #include "../block_scaled_mxfp4_bf16_amd/csrc/workspace_pool.hpp"
 
+static std::mutex g_mu;  // the fake allocator is called from several threads
 static std::set<void *> g_alloced;
+static std::map<void *, size_t> g_size;
 static size_t g_next = 0x10000;
 static bool g_fail = false;
 
 static int fake_alloc(int, void *, size_t bytes, void **out) {
+  std::lock_guard<std::mutex> lk(g_mu);
   if (g_fail) return 4;
   *out = (void *)g_next;
   g_next += (bytes + 4095) & ~(size_t)4095;
   g_alloced.insert(*out);
+  g_size[*out] = bytes;
+  return 0;
+}
+
+// Several threads ask for workspaces on 2 devices x 4 streams at once: every
+// buffer handed out was allocated, holds the request, and the registry's
+// live bytes end equal to the sum of the (device, stream) buffers.
+static int concurrent_check() {
+  mxfp4::WorkspacePool<int (*)(int, void *, size_t, void **)> pool(fake_alloc);
+  std::atomic<int> bad{0};
+  std::vector<std::thread> ts;
+  for (int t = 0; t < 8; ++t) {
+    ts.emplace_back([&, t] {
+      std::mt19937 rng(1234 + t);
+      for (int i = 0; i < 4000; ++i) {
+        const int dev = rng() % 2;
+        void *stream = (void *)(uintptr_t)(1 + rng() % 4);
+        const size_t need = 1 + rng() % (1 << 20);
+        void *p = nullptr;
+        if (pool.get(dev, stream, need, &p) != 0 || p == nullptr) {
+          ++bad;
+          continue;
+        }
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto it = g_size.find(p);
+        if (it == g_size.end() || it->second < need) ++bad;
+      }
+    });
+  }
+  for (auto &th : ts) th.join();
+  if (bad.load() != 0) {
+    fprintf(stderr, "concurrent check: %d bad results\n", bad.load());
+    return 1;
+  }
+  // one live buffer per (device, stream) pair that was used: 8 pairs
+  size_t live = 0;
+  for (int dev = 0; dev < 2; ++dev)
+    for (int s = 1; s <= 4; ++s) {
+      void *p = nullptr;
+      if (pool.get(dev, (void *)(uintptr_t)s, 1, &p) != 0 || p == nullptr) return 1;
+      std::lock_guard<std::mutex> lk(g_mu);
+      live += (g_size[p] + 255) & ~(size_t)255;
+    }
+  if (live != pool.live_bytes()) {
+    fprintf(stderr, "concurrent check: live %zu, registry says %zu\n", live, pool.live_bytes());
+    return 1;
+  }
   return 0;
 }
 
@@ -54,6 +110,7 @@ int main() {
   CHECK(pool.get(0, s1, 1 << 20, &f) == 4 && f == nullptr);
   g_fail = false;
   CHECK(pool.get(0, s1, 512, &p) == 0 && p == r && pool.retired_count() == 2);
+  CHECK(concurrent_check() == 0);
   printf("workspace pool ok\n");
   return 0;
 }
