@@ -307,7 +307,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
     const int mt = t / TN, sub = t % TN;
     const int row = m0 + 16 * mt + 4 * (ln >> 4) + r;
     const int col = 16 * (n_tile * TN + sub) + (ln & 15);
-    if (row < M) C[(size_t)row * N + col] = (uint16_t)f32_to_bf16_rne(v);
+    if (row < M) C[(size_t)row * N + col] = (uint16_t)bf16x2_rne(v, 0.f);
   };
   auto elem = [&](int mt, int nt, int r) { return (((mt * WN + wn) * NT + nt) * 4 + r) * 64 + lane; };
 
@@ -365,10 +365,10 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
         const int col = 16 * (n_tile * TN + sub) + (ln & 15);
         if (row < M) {
           u32x4 pk;
-          pk.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-          pk.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-          pk.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
-          pk.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
+          pk.x = bf16x2_rne(v[0], v[1]);
+          pk.y = bf16x2_rne(v[2], v[3]);
+          pk.z = bf16x2_rne(v[4], v[5]);
+          pk.w = bf16x2_rne(v[6], v[7]);
           *(u32x4 *)(C + (size_t)row * N + col) = pk;
         }
       }
