@@ -26,7 +26,9 @@ The headline is the largest configuration, M=256 N=7168 K=7168, reported as
 TFLOP/s against the dense MXFP4 matrix peak.  Every configuration (the five
 of the method's workloads and the other leaderboard shapes on the pages) is
 reported under per_config with its own roofline block; for context each is
-also timed warm (one set, inputs resident in L2 and the MALL).
+also timed warm (one set, inputs resident in L2 and the MALL), and the five
+method workloads from an A quantized beforehand (mxfp4_gemm_q, cold, under
+per_config.<workload>.prequantized_a).
 
 Prints one JSON line.
 """
@@ -332,6 +334,56 @@ def time_config(torch, mx, w, steps, warmup, samples, cold=True, clocks_under_lo
     if load_clocks is not None:
         r["clocks_under_load"] = load_clocks
     return r
+
+
+def time_config_q(torch, mx, w, steps, samples):
+    """The pre-quantized-A entry point (mxfp4_gemm_q) on the workload: A is
+    quantized once, outside the timed region, to codes and shuffled scales
+    (the form a caller that reuses one A quantization across GEMMs holds),
+    and the calls cycle cold through buffer sets as in time_config.  Median,
+    p10 and p90 over `samples` replays of a graph of whole rotations."""
+    import numpy as np
+    M, N, K = w.M, w.N, w.K
+    dev = torch.device("cuda", 0)
+    a = torch.from_numpy(w.a_bits().view(np.int16)).view(torch.bfloat16).to(dev)
+    b = torch.from_numpy(w.b_bits().view(np.int16)).view(torch.bfloat16).to(dev)
+    qb, sb = mx.quantize(b)
+    bw, bs = mx.preshuffle_b(qb, sb)
+    aq, as_ = mx.quantize(a, shuffled_scales=True)
+    del a, b, qb, sb
+    per_set = aq.numel() + as_.numel() + bw.numel() + bs.numel() + 2 * M * N
+    sets, _ = rotation(per_set, steps)
+    bufs = [(aq, as_, bw, bs)] + [(aq.clone(), as_.clone(), bw.clone(), bs.clone()) for _ in range(sets - 1)]
+    bufs = [t + (torch.empty((M, N), dtype=torch.bfloat16, device=dev),) for t in bufs]
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        mx.mxfp4_reserve(M, N, K, stream=stream)
+        for i in range(3):
+            mx.mxfp4_gemm_q(*bufs[i % sets], M, N, K, stream=stream)
+    stream.synchronize()
+    rounds = max(1, math.ceil(200 / sets))
+    calls = rounds * sets
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(calls):
+            mx.mxfp4_gemm_q(*bufs[i % sets], M, N, K, stream=stream)
+    with torch.cuda.stream(stream):
+        g.replay()  # upload
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
+    with torch.cuda.stream(stream):
+        for k in range(samples):
+            ev[k][0].record(stream)
+            g.replay()
+            ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    us = [x.elapsed_time(y) * 1e3 / calls for x, y in ev]
+    del g, bufs
+    torch.cuda.empty_cache()
+    med = percentile(us, 50)
+    return {"schedule": mx.mxfp4_gemm_q_schedule_name(M, N, K), "us_per_call": round(med, 4),
+            "us_p10": round(percentile(us, 10), 4), "us_p90": round(percentile(us, 90), 4),
+            "tflops": alg_flops(M, N, K) / (med * 1e-6) / 1e12, "buffer_sets": sets, "set_bytes": per_set}
 
 
 def time_prepare_b(torch, mx, w, steps=50):
@@ -875,6 +927,8 @@ def main():
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the second, warm timing (one buffer set, so inputs stay in L2 and MALL)")
     ap.add_argument("--no-clocks", action="store_true", help="skip reading the GPU clocks with amd-smi")
+    ap.add_argument("--no-gemm-q", action="store_true",
+                    help="skip timing mxfp4_gemm_q (A quantized beforehand) on the five method workloads")
     ap.add_argument("--floors", action="store_true",
                     help="measure the machine's floors with the probe library instead (launch, B streaming, "
                          "matrix-instruction rate and clock, and the per-phase timing of the small-M kernel for "
@@ -921,6 +975,12 @@ def main():
             # context only: the same calls on one buffer set, inputs warm in L2 and MALL
             r["warm_us_per_call"] = time_config(torch, mx, w, args.steps, args.warmup, args.samples,
                                                 cold=False)["us_per_call"]
+        if not args.no_gemm_q and name in ("c1", "c2", "c3", "c4", "c5"):
+            # context: the same product from an A quantized beforehand
+            r["prequantized_a"] = time_config_q(torch, mx, w, args.steps, args.samples)
+            print("[bench] %s from pre-quantized A (mxfp4_gemm_q): %.3f us/call cold, schedule %s"
+                  % (w.name, r["prequantized_a"]["us_per_call"], r["prequantized_a"]["schedule"]),
+                  file=sys.stderr, flush=True)
         per[w.name] = r
         print("[bench] %s: %.3f us/call cold (p10 %.3f, p90 %.3f%s), %.1f TFLOP/s, %.0f GB/s, %.1f%% of %s "
               "roofline, schedule %s"

@@ -69,7 +69,8 @@ namespace mxfp4 {
 // [workgroups * waves][8].  Split-1 schedules only.
 template <int MT, int NT, int WN, int WK, int KPW, bool PREQ, int RB, int EPI, bool STAMPS = false>
 __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__restrict__ A,
-                                                           const uint8_t *__restrict__ Aop,
+                                                           const uint8_t *__restrict__ Aq,
+                                                           const uint8_t *__restrict__ As,
                                                            const uint8_t *__restrict__ Bw,
                                                            const uint8_t *__restrict__ Bs, uint16_t *__restrict__ C,
                                                            float *__restrict__ partials,
@@ -164,20 +165,27 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
       aw[u] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off_or_oob(ok, (row * K + kel) * 2), 0, 0);
     }
   } else {
-    // pre-quantized A in operand blocks: per (m tile, step) 1 KiB of codes,
-    // lane L's 16 bytes at 16*L, then 64 scale bytes
-    const int op_bytes = ((M + 15) >> 4) * KS * 1088;
-    const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Aop, 0, op_bytes, kRsrcWord3);
+    // pre-quantized A as the caller holds it: codes [M, K/2] row-major and
+    // scales in the shuffled layout (B's).  Operand lane l takes the 16 code
+    // bytes of row 16*mtile + l%16, K chunk l/16 of the step (the two steps
+    // of a 128-byte row segment come from two loads), and the scale dword at
+    // lane l of the step pair's 256-byte block, as for B.
+    const int q_bytes = M * (K >> 1);
+    const int as_bytes = ((M + 255) >> 8) * 8 * gp * 32;
+    const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Aq, 0, q_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t as_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)As, 0, as_bytes, kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < KPW; ++i) {
       const int ks = S0 + wk * KPW + i;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int mtile = m_tile * MT + mt;
-        const bool ok = (ks < S1) && (mtile * 16 < M);
-        const int blk = (mtile * KS + ks) * 1088;
-        ap[i][mt] = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, off_or_oob(ok, blk + lane * 16), 0, 0);
-        asb[i][mt] = __builtin_amdgcn_raw_buffer_load_b8(q_rsrc, off_or_oob(ok, blk + 1024 + lane), 0, 0);
+        const int row = mtile * 16 + (lane & 15);
+        const bool ok = (ks < S1) && (row < M) && (ks * 128 + kc * 32 < K);
+        ap[i][mt] = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, off_or_oob(ok, row * (K >> 1) + ks * 64 + kc * 16), 0, 0);
+        const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(
+            as_rsrc, off_or_oob(ks < S1, (mtile >> 1) * gp * 32 + (ks >> 1) * 256 + lane * 4), 0, 0);
+        asb[i][mt] = (w >> (8 * ((mtile & 1) | ((ks & 1) << 1)))) & 0xFFu;
       }
     }
   }
@@ -480,10 +488,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
   }
 }
 
-// Operand preparation for the pre-quantized mode (quantize A, or repack
-// pre-quantized A, into operand blocks at `aop`) and the zero fill of the
-// float-atomic epilogue's tiles; defined in gemm_kernels.hip.
-hipError_t launch_operand_prep(const GemmArgs &a, uint8_t *aop, bool sw, hipStream_t stream);
+// The zero fill of the float-atomic epilogue's tiles (gemm_kernels.hip).
 hipError_t launch_zero_f32(float *p, int n4, hipStream_t stream);
 
 typedef hipError_t (*launch_fn)(const GemmArgs &, int split, bool sw, hipStream_t);
@@ -493,12 +498,23 @@ hipError_t launch_variant(const GemmArgs &a, int split, bool sw, hipStream_t str
   const int n_tiles = a.N / (16 * NT * WN);
   const int m_tiles = (a.M + 16 * MT - 1) / (16 * MT);
   char *ws = (char *)a.workspace;
-  uint8_t *aop = nullptr;
+  const uint8_t *aq = nullptr, *as = nullptr;
   if (!PREQ && a.Aq) return hipErrorInvalidValue;  // pre-quantized A needs a pre-quantized schedule
   if (PREQ) {
-    aop = (uint8_t *)(ws + kTicketBytes);
-    hipError_t e = launch_operand_prep(a, aop, sw, stream);
-    if (e != hipSuccess) return e;
+    if (a.Aq) {
+      // the caller's codes and shuffled scales, read as they are: one launch
+      aq = (const uint8_t *)a.Aq;
+      as = (const uint8_t *)a.As;
+    } else {
+      // bf16 A under a pre-quantized schedule: quantize it into the
+      // workspace first, in the caller's layout
+      uint8_t *q = (uint8_t *)(ws + kTicketBytes);
+      uint8_t *sc = q + caller_codes_bytes(a.M, a.K);
+      hipError_t e = launch_quantize(a.A, a.M, a.K, q, sc, true, sw, stream);
+      if (e != hipSuccess) return e;
+      aq = q;
+      as = sc;
+    }
   }
   uint32_t *tickets = (uint32_t *)ws;
   float *partials = nullptr;
@@ -511,8 +527,8 @@ hipError_t launch_variant(const GemmArgs &a, int split, bool sw, hipStream_t str
   }
   dim3 grid((unsigned)(EPI == 2 ? split : n_tiles * m_tiles * split));
   gemm_kernel<MT, NT, WN, WK, KPW, PREQ, RB, EPI><<<grid, 64 * WN * WK, 0, stream>>>(
-      (const uint16_t *)a.A, aop, (const uint8_t *)a.Bw, (const uint8_t *)a.Bs, (uint16_t *)a.C, partials, tickets, a.M,
-      a.N, a.K, split, n_tiles, sw ? 1 : 0);
+      (const uint16_t *)a.A, aq, as, (const uint8_t *)a.Bw, (const uint8_t *)a.Bs, (uint16_t *)a.C, partials, tickets,
+      a.M, a.N, a.K, split, n_tiles, sw ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
-// Fused MXFP4 GEMM: the operand-preparation and fill kernels, the joined
-// variant table and its queries.  The kernel template itself, with its full
+// Fused MXFP4 GEMM: the fill kernel, the joined variant table and its
+// queries.  The kernel template itself, with its full
 // description, is in gemm_fused.hpp; its instantiations are spread over
 // gemm_table_*.hip.
 #include <vector>
@@ -22,71 +22,6 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream) {
   if (n4 == 0) return hipSuccess;
   if (n4 > (size_t)INT32_MAX - 255) return hipErrorInvalidValue;
   zero_f32_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, stream>>>((float *)p, (int)n4);
-  return hipGetLastError();
-}
-
-// A quantized once into operand blocks for the pre-quantized mode: block
-// (m tile, step) holds 1 KiB of codes (operand lane L's 16 bytes at 16*L)
-// and 64 scale bytes.  One wave per 16 rows x 32 elements, four consecutive
-// lanes per group, as in the staging of the fused mode.
-__global__ __launch_bounds__(64) void quant_operand_kernel(const uint16_t *__restrict__ A, uint8_t *__restrict__ Aop,
-                                                           int M, int K, int units, int sw_quant) {
-  const int lane = threadIdx.x;
-  const int unit = blockIdx.x;  // (m tile, step, chunk), chunk fastest; one wave per workgroup
-  if (unit >= units) return;
-  const int KS = (K + 127) >> 7;
-  const int ch = unit & 3;
-  const int ks = (unit >> 2) % KS;
-  const int mtile = (unit >> 2) / KS;
-  const int row = mtile * 16 + (lane >> 2);
-  const int kel = ks * 128 + ch * 32 + (lane & 3) * 8;
-  const int a_bytes = M * K * 2;
-  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, a_bytes, kRsrcWord3);
-  const bool ok = (row < M) && (ks * 128 + ch * 32 < K);
-  const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ok ? (row * K + kel) * 2 : a_bytes, 0, 0);
-  uint32_t s;
-  const uint32_t d = quant_quarter(w, sw_quant, &s);
-  uint8_t *blk = Aop + (size_t)(mtile * KS + ks) * 1088;
-  ((uint32_t *)blk)[ch * 64 + lane] = d;
-  if ((lane & 3) == 0) blk[1024 + ch * 16 + (lane >> 2)] = (uint8_t)s;
-}
-
-// Pre-quantized A (codes [M, K/2] as mxfp4_quantize writes them, scales
-// in the shuffled layout) -> operand blocks.  One single-wave workgroup per
-// (16-row tile t, step ks): operand lane L takes the 16 code bytes of row
-// 16t + L%16, K chunk 4ks + L/16, and that group's scale byte.  Rows past M
-// and chunks past K become zero codes with scale byte 0, as quantizing
-// zeros would give.
-__global__ __launch_bounds__(64) void repack_operand_kernel(const uint8_t *__restrict__ Aq,
-                                                            const uint8_t *__restrict__ As,
-                                                            uint8_t *__restrict__ Aop, int M, int K) {
-  const int lane = threadIdx.x;
-  const int KS = (K + 127) >> 7;
-  const int t = blockIdx.x / KS, ks = blockIdx.x - (blockIdx.x / KS) * KS;
-  const int G = K >> 5, gp = (G + 7) & ~7;
-  const int row = 16 * t + (lane & 15), grp = 4 * ks + (lane >> 4);
-  const bool ok = row < M && grp < G;
-  const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)Aq, 0, M * (K >> 1), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t s_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void *)As, 0, ((M + 255) & ~255) * gp, kRsrcWord3);
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, off_or_oob(ok, row * (K >> 1) + grp * 16), 0, 0);
-  const uint32_t sc =
-      __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, off_or_oob(ok, (int)shuffled_scale_offset(row, grp, gp)), 0, 0);
-  uint8_t *blk = Aop + (size_t)(t * KS + ks) * 1088;
-  *(u32x4 *)(blk + lane * 16) = v;
-  blk[1024 + lane] = (uint8_t)sc;
-}
-
-size_t operand_a_bytes(int M, int K) { return (size_t)((M + 15) / 16) * (size_t)((K + 127) / 128) * 1088; }
-
-hipError_t launch_operand_prep(const GemmArgs &a, uint8_t *aop, bool sw, hipStream_t stream) {
-  if (a.Aq) {
-    const int blocks = ((a.M + 15) / 16) * ((a.K + 127) / 128);
-    repack_operand_kernel<<<blocks, 64, 0, stream>>>((const uint8_t *)a.Aq, (const uint8_t *)a.As, aop, a.M, a.K);
-  } else {
-    const int units = ((a.M + 15) / 16) * ((a.K + 127) / 128) * 4;
-    quant_operand_kernel<<<units, 64, 0, stream>>>((const uint16_t *)a.A, aop, a.M, a.K, units, sw ? 1 : 0);
-  }
   return hipGetLastError();
 }
 

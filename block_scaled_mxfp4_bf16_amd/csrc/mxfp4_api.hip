@@ -85,6 +85,15 @@ const Tuned kTuned[] = {
     {16, 2112, 7168, "mt1_nt1_wn4_wk4_kpw4_split4"},
     {32, 2880, 512, "mt1_nt1_wn4_wk1_kpw4_split1"},
     {256, 3072, 1536, "mt2_nt2_wn3_wk4_kpw3_split1"},
+    // A given quantized (mxfp4_gemm_q); the large-M entry above serves it too
+    {16, 3072, 1536, "mt1_nt1_wn1_wk8_kpw2_split1_pq"},
+    {32, 4096, 512, "mt1_nt2_wn1_wk4_kpw1_split1_pq"},
+    {8, 2112, 7168, "mt1_nt1_wn1_wk16_kpw4_split1_pq"},
+    {64, 7168, 2048, "mt4_nt2_wn1_wk4_kpw4_split1_pq"},
+    {4, 2880, 512, "mt1_nt2_wn1_wk4_kpw1_split1_pq"},
+    {16, 2112, 7168, "mt1_nt1_wn1_wk16_kpw4_split1_pq"},
+    {32, 2880, 512, "mt1_nt2_wn1_wk4_kpw1_split1_pq"},
+    {256, 3072, 1536, "mt2_nt2_wn1_wk4_kpw4_split1_pq"},
 };
 
 // Estimated cost of a large-M schedule, in log-microseconds on the same
@@ -133,7 +142,9 @@ bool pick_wide(int M, int N, int K, Schedule *out, double *cost_out = nullptr) {
 // Estimated cost of a fused schedule, in log-microseconds.
 // A CU keeps only ~64 lines (128 bytes) outstanding to L2, so a workgroup's
 // time grows with the lines it requests: A rows actually present (bf16, or
-// codes when A arrives quantized), B columns and B scales, over its K run;
+// codes when A arrives quantized -- read in 64-byte halves of their lines,
+// one per step, so twice the lines of their bytes), B columns and B scales,
+// over its K run;
 // workgroups beyond one per CU queue behind others.  A split of K across
 // workgroups costs its epilogue.  The weights were fitted to cold,
 // graph-replayed timings of every compiled schedule on twelve decode shapes
@@ -145,7 +156,7 @@ double fused_cost(const Schedule &s, int M, int N, int K, bool quantized_a, doub
   const double rows = M < 16 * s.mt ? M : 16 * s.mt;
   const double cols = 16.0 * s.nt * s.wn;
   const double wgs = (double)tiles_of(s, M, N) * s.split;
-  const double a_lines = rows * per * (quantized_a ? 0.5 : 2.0);
+  const double a_lines = rows * per * (quantized_a ? 1.0 : 2.0);
   const double lines = a_lines + cols * per * 0.5 + cols / 32.0 * per * 2.0;
   const double per_cu = std::ceil(wgs / 256.0) * lines;
   *pad = (double)(s.wk * s.kpw - per) / (s.wk * s.kpw);
@@ -155,8 +166,10 @@ double fused_cost(const Schedule &s, int M, int N, int K, bool quantized_a, doub
 bool pick_schedule(int M, int N, int K, Schedule *out, bool need_pq = false) {
   for (const Tuned &t : kTuned)
     if (t.M == M && t.N == N && t.K == K) {
+      // an entry serves the mode it was tuned for; large-M entries serve both
+      // (that kernel reads A quantized in either case)
       Schedule s;
-      if (parse_name(t.name, &s) && covers(s, M, N, K) && (s.pq || !need_pq)) {
+      if (parse_name(t.name, &s) && covers(s, M, N, K) && (s.wide || s.pq == (need_pq ? 1 : 0))) {
         *out = s;
         return true;
       }

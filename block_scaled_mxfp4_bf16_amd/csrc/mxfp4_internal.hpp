@@ -15,8 +15,10 @@ namespace mxfp4 {
 //   kpw   128-wide K steps per wave (a workgroup covers wk*kpw steps)
 //   split workgroups that split K for one output tile; the last to finish
 //         adds the partial sums from the workspace and stores C
-//   pq    1: A is quantized once by a separate launch into operand blocks in
-//         the workspace and the GEMM reads those; 0: the GEMM quantizes A
+//   pq    1: the GEMM reads A already quantized, in the caller's layout
+//         (codes [M, K/2] and shuffled scales): mxfp4_gemm_q's A as it is, or
+//         bf16 A quantized into the workspace by a launch of its own; 0: the
+//         GEMM quantizes A
 //   rb    rows per staged A block: 16, or 8 (for M <= 8: no loads or
 //         converts are spent on rows that do not exist)
 //   wide  1: the large-M kernel -- A quantized once, wk waves per
@@ -61,13 +63,17 @@ int num_gemm_variants();
 void gemm_variant_shape(int v, Schedule *s);  // fills everything but split
 int find_gemm_variant(int mt, int nt, int wn, int wk, int kpw, int pq, int rb, int wide, int epi = 0);
 
-// Bytes of pre-quantized A in the workspace: the larger of the two operand
-// layouts (the fused kernels' 1088-byte blocks, the large-M kernel's
-// quad-packed one), so one workspace size serves either.
-size_t operand_a_bytes(int M, int K);
+// Bytes of quantized A in the workspace: the larger of the two layouts
+// (the caller's -- codes, 256-byte aligned, then shuffled scales with rows
+// padded to 256 -- and the large-M kernel's quad-packed one), so one
+// workspace size serves either.
+inline size_t caller_codes_bytes(int M, int K) { return ((size_t)M * (K / 2) + 255) & ~(size_t)255; }
+inline size_t caller_a_bytes(int M, int K) {
+  return caller_codes_bytes(M, K) + (size_t)((M + 255) & ~255) * (size_t)(((K / 32) + 7) & ~7);
+}
 size_t quad_operand_bytes(int M, int K);
 inline size_t pq_operand_bytes(int M, int K) {
-  const size_t a = operand_a_bytes(M, K), b = quad_operand_bytes(M, K);
+  const size_t a = caller_a_bytes(M, K), b = quad_operand_bytes(M, K);
   return a > b ? a : b;
 }
 

@@ -29,8 +29,8 @@ int launch_stamped(const void *A, const void *Bw, const void *Bs, void *C, void 
   const size_t grid = (size_t)n_tiles * m_tiles;
   if (stamp_words < grid * WN * WK * 8) return 3;
   mxfp4::gemm_kernel<MT, NT, WN, WK, KPW, false, RB, 0, true><<<(unsigned)grid, 64 * WN * WK, 0, stream>>>(
-      (const uint16_t *)A, nullptr, (const uint8_t *)Bw, (const uint8_t *)Bs, (uint16_t *)C, (float *)stamps, nullptr,
-      M, N, K, 1, n_tiles, sw ? 1 : 0);
+      (const uint16_t *)A, nullptr, nullptr, (const uint8_t *)Bw, (const uint8_t *)Bs, (uint16_t *)C, (float *)stamps,
+      nullptr, M, N, K, 1, n_tiles, sw ? 1 : 0);
   return (int)hipGetLastError();
 }
 

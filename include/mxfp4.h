@@ -139,7 +139,9 @@ MXFP4_API mxfp4_status_t mxfp4_prepare_b(const void *b_bf16, int64_t N, int64_t 
 /* A with a standalone kernel and hands FP4 A and its shuffled scales to the */
 /* GEMM for large M; mxfp4_quantize with shuffled_scales = 1 writes exactly  */
 /* these inputs.)  Same C as mxfp4_gemm on the bf16 A when both run the same */
-/* pre-quantized schedule; only such schedules run here.                     */
+/* pre-quantized schedule; only such schedules run here.  Below 256 rows     */
+/* the GEMM reads Aq and As as they are, in one launch; the large-M kernel   */
+/* first repacks them into its own operand layout in the workspace.          */
 /*   Aq      [M, K/2] packed e2m1, natural layout, 16-byte aligned (input)   */
 /*   As      shuffled scales, mxfp4_shuffled_scale_bytes(M, K) bytes (input) */
 /*   Bq_sh, Bs_sh, C, M, N, K, stream: as mxfp4_gemm                         */

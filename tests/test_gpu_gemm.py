@@ -108,7 +108,8 @@ SCHEDULES = ["mt1_nt1_wn1_wk1_kpw1_split17", "mt1_nt1_wn1_wk4_kpw1_split5", "mt1
              "mt1_nt1_wn4_wk4_kpw2_split3", "mt1_nt1_wn1_wk16_kpw2_split1", "mt2_nt1_wn4_wk2_kpw2_split5",
              "mt2_nt2_wn2_wk4_kpw1_split5", "mt4_nt1_wn8_wk1_kpw2_split9", "mt4_nt2_wn4_wk1_kpw2_split9",
              "mt4_nt1_wn2_wk4_kpw2_split3", "mt4_nt2_wn1_wk2_kpw2_split5",
-             # A quantized once by its own launch into operand blocks
+             # pre-quantized mode: here bf16 A is quantized into the workspace by a launch of its
+             # own, in the caller's layout, which the GEMM then reads
              "mt4_nt2_wn2_wk2_kpw4_split3_pq", "mt1_nt1_wn2_wk8_kpw1_split3_pq", "mt8_nt1_wn2_wk2_kpw4_split3_pq",
              "mt2_nt2_wn1_wk1_kpw4_split5_pq", "mt4_nt4_wn1_wk2_kpw4_split3_pq",
              # large-M kernel: waves split K, A quantized once
@@ -431,12 +432,13 @@ def test_gemm_q_equals_gemm_under_the_same_schedule(sched, M, N, K):
     assert_close(cq, c.ref(), sched)
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"] + list(syn.EXTRA_SHAPES))
 def test_gemm_q_default_schedule_on_oracle_quantized_a(name):
     """mxfp4_gemm_q fed the oracle's own quantized A (codes and shuffled
-    scales) under its default schedule matches the oracle's product."""
+    scales) under its default schedule matches the oracle's product, every
+    output compared."""
     torch = torch_cuda()
-    w = syn.CONFIGS[name]
+    w = syn.CONFIGS.get(name) or syn.EXTRA_SHAPES[name]
     c = Case(torch, w.a_bits(), w.b_bits())
     qa, sa = oracle.quantize(c.a_bits)
     aq = to_dev_u8(torch, qa)
