@@ -16,16 +16,18 @@
 // A is quantized inside the kernel (submission 608632, kernel v7, does the
 // same per BLOCK_K tile with the hardware convert) and staged through LDS,
 // once per workgroup, in the operand layout:
-//   - one load instruction covers 16 rows x one 32-element group: four
-//     consecutive lanes read one group's 64 contiguous bytes, so the access
-//     is coalesced (the operand layout read straight from memory would give
-//     every lane its own 64-byte run);
+//   - one load instruction covers 8 rows x two 32-element groups: eight
+//     consecutive lanes read one row's 128 contiguous bytes, a whole cache
+//     line, so no line is requested twice (the vector cache does not merge
+//     two requests for one line in flight).  Schedules of one row tile and
+//     one column wave load 16 rows x one group instead (four lanes per
+//     64-byte run), whose LDS writes are conflict-free;
 //   - the four lanes of a group combine their amax with two DPP steps, then
 //     each converts its 8 elements with v_cvt_scalef32_pk_fp4_bf16 into one
 //     dword of codes;
-//   - lane t writes its dword at dword t of a 1 KiB block and the scale at
-//     byte t/4 + 16*kc; a block is exactly one matrix operand (operand lane L
-//     reads 16 bytes at 16*L), and both sides are free of bank conflicts.
+//   - the lane of row r, group c, quarter q writes its dword at dword
+//     64c + 4r + q of a 1 KiB block and the scale at byte 16c + r; a block
+//     is exactly one matrix operand (operand lane L reads 16 bytes at 16*L).
 //
 // Work split: a workgroup owns an output tile of 16*MT rows x 16*NT*WN
 // columns and a run of K steps.  Its waves form a WN x WK grid: WN waves
@@ -82,6 +84,10 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
   // staged A blocks: 16 rows x 32 elements each, or (RB == 8, for M <= 8)
   // 8 rows x 64 elements, so that no load is spent on rows that do not exist
   constexpr int UPS = RB == 8 ? 2 : 4;              // blocks per (step, m tile)
+  // Whole-line A loads (below).  Their LDS writes conflict two ways, which
+  // shows where a single wave stages one tile and uses it at once (one row
+  // tile, one column wave); there the half-line order is kept.
+  constexpr bool LINES = RB == 8 || MT > 1 || WN > 1;
   constexpr int UNITS = KW * MT * UPS;
   constexpr int UPW = (UNITS + WAVES - 1) / WAVES;  // per wave
   constexpr int TN = NT * WN;                       // 16-column subtiles per workgroup
@@ -152,14 +158,18 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
   if constexpr (!PREQ) {
 #pragma unroll
     for (int u = 0; u < UPW; ++u) {
-      // (step, m tile, chunk) with the chunk fastest; with one wave per
-      // column group each wave stages exactly the blocks of its own steps
+      // (step, m tile, row half, chunk pair) with the chunk pair fastest
+      // (LINES): lane t loads 16 bytes of row 8*half + t/8, chunk
+      // 2*pair + (t/4)%2, so eight lanes read one row's 128-byte line whole;
+      // else (step, m tile, chunk): lane t loads row t/4, chunk unit%4.
+      // With one wave per column group each wave stages exactly the blocks
+      // of its own steps.
       const int unit = WN == 1 ? wk * (KPW * MT * UPS) + u : wave + u * WAVES;
       const int st = unit / (MT * UPS);
       const int mt = (unit / UPS) % MT;
-      const int ch = RB == 8 ? 2 * (unit & 1) + ((lane >> 2) & 1) : (unit & 3);
+      const int ch = LINES ? 2 * (unit & 1) + ((lane >> 2) & 1) : (unit & 3);
       const int ks = S0 + st;
-      const int row = m0 + 16 * mt + (RB == 8 ? (lane >> 3) : (lane >> 2));
+      const int row = m0 + 16 * mt + (LINES ? (RB == 8 ? 0 : 8 * ((unit >> 1) & 1)) + (lane >> 3) : (lane >> 2));
       const int kel = ks * 128 + ch * 32 + (lane & 3) * 8;
       const bool ok = (unit < UNITS) && (ks < S1) && (row < M) && (ks * 128 + ch * 32 < K);
       aw[u] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off_or_oob(ok, (row * K + kel) * 2), 0, 0);
@@ -222,17 +232,13 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint16_t *__re
         if (UPW * WAVES == UNITS || unit < UNITS) {
           uint32_t s;
           const uint32_t d = quant_quarter_t<SW>(aw[u], &s);
-          if constexpr (RB == 8) {
-            // lane t: row t/8, chunk 2*(unit&1) + (t/4)%2, quarter t%4
-            const int blk = unit >> 1;
-            const int ch = 2 * (unit & 1) + ((lane >> 2) & 1);
-            const int r = lane >> 3;
-            a_lds[blk * 256 + ch * 64 + r * 4 + (lane & 3)] = d;
-            if ((lane & 3) == 0) s_lds[blk * 64 + ch * 16 + r] = (uint8_t)s;
-          } else {
-            a_lds[unit * 64 + lane] = d;
-            if ((lane & 3) == 0) s_lds[(unit >> 2) * 64 + (unit & 3) * 16 + (lane >> 2)] = (uint8_t)s;
-          }
+          // the lane's row, group and quarter of the block's 16 x 128 operand
+          // (as loaded above)
+          const int blk = RB == 8 ? unit >> 1 : unit >> 2;
+          const int ch = LINES ? 2 * (unit & 1) + ((lane >> 2) & 1) : (unit & 3);
+          const int r = LINES ? (RB == 8 ? 0 : 8 * ((unit >> 1) & 1)) + (lane >> 3) : (lane >> 2);
+          a_lds[blk * 256 + ch * 64 + r * 4 + (lane & 3)] = d;
+          if ((lane & 3) == 0) s_lds[blk * 64 + ch * 16 + r] = (uint8_t)s;
         }
       }
     };
