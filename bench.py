@@ -529,15 +529,16 @@ def summarize_pmc(fetch_dir, write_dir, command):
     print(json.dumps(out))
 
 
-def kernel_signature(w):
-    """The GEMM kernel instantiation the library runs for a workload, as the
-    profiler names it (without namespace): gemm_kernel<MT, NT, WN, WK, KPW,
-    pre-quantized, staged rows, epilogue, phase stamps (always off)> or
+def kernel_signature(w, quantized_a=False):
+    """The GEMM kernel instantiation the library runs for a workload (with
+    quantized_a: the call of mxfp4_gemm_q), as the profiler names it
+    (without namespace): gemm_kernel<MT, NT, WN, WK, KPW, pre-quantized,
+    staged rows, epilogue, phase stamps (always off)> or
     gemm_wide_kernel<MW, NW, W, D, LDS-staged B, phase stamps (always off)>,
     read off the schedule name."""
     import re
     import block_scaled_mxfp4_bf16_amd as mx
-    name = mx.mxfp4_gemm_schedule_name(w.M, w.N, w.K)
+    name = (mx.mxfp4_gemm_q_schedule_name if quantized_a else mx.mxfp4_gemm_schedule_name)(w.M, w.N, w.K)
     m = re.match(r"(wide|widel)_mt(\d+)_nt(\d+)_w(\d+)_d(\d+)_split\d+$", name)
     if m:
         return "gemm_wide_kernel<%s, %s, %s, %s, %s, false>" % (m.group(2), m.group(3), m.group(4), m.group(5),
@@ -571,6 +572,10 @@ def summarize_mfma(pmc_dir, configs, command):
     for c in configs:
         w = syn.CONFIGS.get(c) or syn.EXTRA_SHAPES[c]
         by_sig.setdefault(kernel_signature(w), []).append((expected_mfma(w.M, w.N, w.K), w.name))
+        # the bench times mxfp4_gemm_q on the five configurations only
+        if c in syn.CONFIGS and kernel_signature(w, True) != kernel_signature(w):
+            by_sig.setdefault(kernel_signature(w, True), []).append(
+                (expected_mfma(w.M, w.N, w.K), w.name + " (A pre-quantized)"))
 
     def workload_of(kernel, inst):
         # the instantiation, then the instruction count where workloads share

@@ -60,21 +60,25 @@ def test_summarize_mfma_on_synthetic_counters(tmp_path, capsys):
         d = 10 + i
         rows += [(d, 65536, wide, "SQ_INSTS_MFMA", 401408, 1000, 1000 + ns),
                  (d, 65536, wide, "SQ_VALU_MFMA_BUSY_CYCLES", 401408 * 16, 1000, 1000 + ns)]
+    fused_q = "void mxfp4::gemm_kernel<1, 2, 1, 4, 1, true, 16, 0, false>(unsigned short const*)"  # c2, gemm_q
     rows += [(20, 32768, fused, "SQ_INSTS_MFMA", 2048, 0, 4000),
              (20, 32768, fused, "SQ_VALU_MFMA_BUSY_CYCLES", 2048 * 16, 0, 4000),
+             (22, 32768, fused_q, "SQ_INSTS_MFMA", 2048, 0, 3000),
+             (22, 32768, fused_q, "SQ_VALU_MFMA_BUSY_CYCLES", 2048 * 16, 0, 3000),
              (21, 57344, quant, "SQ_INSTS_MFMA", 0, 0, 3000)]  # not a GEMM: ignored
     write_counters(str(tmp_path / "pmc"), rows)
     bench.summarize_mfma(str(tmp_path / "pmc"), ["c2", "c5"], "cmd")
     out = json.loads(capsys.readouterr().out)
     assert out["command"] == "cmd"
     ks = {k["kernel"]: k for k in out["kernels"]}
-    assert set(ks) == {wide.split("(")[0], fused.split("(")[0]}
+    assert set(ks) == {wide.split("(")[0], fused.split("(")[0], fused_q.split("(")[0]}
     w = ks[wide.split("(")[0]]
     assert w["dispatches"] == 3 and w["mfma_instructions"] == 401408
     assert w["workload"] == syn.CONFIGS["c5"].name
     assert w["busy_cycles_per_instruction"] == 16.0 and w["duration_ns"] == 16400
     assert w["matrix_busy_frac_at_2400MHz"] == pytest.approx(401408 * 16 / (1024 * 2.4 * 16400), abs=1e-4)
     assert ks[fused.split("(")[0]]["workload"] == syn.CONFIGS["c2"].name
+    assert ks[fused_q.split("(")[0]]["workload"] == syn.CONFIGS["c2"].name + " (A pre-quantized)"
 
 
 def test_summarize_pmc_scales_by_the_copy_calibration(tmp_path, monkeypatch, capsys):
