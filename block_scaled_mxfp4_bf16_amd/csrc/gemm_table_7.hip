@@ -20,6 +20,10 @@ static const Variant kPart[] = {
     VQ(8, 1, 2, 1, 4), VQ(8, 1, 2, 2, 1), VQ(8, 1, 2, 2, 2), VQ(8, 1, 2, 2, 4), VQ(8, 2, 1, 1, 1), VQ(8, 2, 1, 1, 2),
     VQ(8, 2, 1, 1, 4), VQ(8, 2, 1, 2, 1), VQ(8, 2, 1, 2, 2), VQ(8, 2, 1, 2, 4), VQ(8, 2, 2, 1, 1), VQ(8, 2, 2, 1, 2),
     VQ(8, 2, 2, 1, 4),
+    // pre-quantized A, long K at M <= 16 without a K split: 8 waves of 8
+    // steps (K up to 8192), faster at K 7168 than 16 waves of 4 (no
+    // quantization to spread over the waves)
+    VQ(1, 1, 1, 8, 8),
 };
 // (a host function: the device pass compiles the kernels the table names,
 // but emits no reference to the host launchers)

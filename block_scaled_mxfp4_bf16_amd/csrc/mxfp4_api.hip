@@ -88,10 +88,10 @@ const Tuned kTuned[] = {
     // A given quantized (mxfp4_gemm_q); the large-M entry above serves it too
     {16, 3072, 1536, "mt1_nt1_wn1_wk8_kpw2_split1_pq"},
     {32, 4096, 512, "mt1_nt2_wn1_wk4_kpw1_split1_pq"},
-    {8, 2112, 7168, "mt1_nt1_wn1_wk16_kpw4_split1_pq"},
+    {8, 2112, 7168, "mt1_nt1_wn1_wk8_kpw8_split1_pq"},
     {64, 7168, 2048, "mt4_nt2_wn1_wk4_kpw4_split1_pq"},
     {4, 2880, 512, "mt1_nt2_wn1_wk4_kpw1_split1_pq"},
-    {16, 2112, 7168, "mt1_nt1_wn1_wk16_kpw4_split1_pq"},
+    {16, 2112, 7168, "mt1_nt1_wn1_wk8_kpw8_split1_pq"},
     {32, 2880, 512, "mt1_nt2_wn1_wk4_kpw1_split1_pq"},
     {256, 3072, 1536, "mt2_nt2_wn1_wk4_kpw4_split1_pq"},
 };
