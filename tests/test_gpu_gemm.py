@@ -410,7 +410,10 @@ def test_graph_replays_match_eager(sched, M, N, K):
 GEMM_Q_CASES = [("mt4_nt1_wn2_wk4_kpw4_split1_pq", 64, 7168, 2048), ("mt1_nt1_wn1_wk8_kpw4_split2_pq", 8, 2112, 7168),
                 ("mt2_nt1_wn1_wk1_kpw4_split1_pq", 32, 4096, 512), ("mt4_nt2_wn2_wk2_kpw4_split3_pq", 40, 256, 2112),
                 ("wide_mt4_nt7_w4_d2_split1", 130, 224, 1088), ("wide_mt8_nt2_w8_d2_split2", 200, 128, 1600),
-                ("wide_mt4_nt1_w8_d4_split3", 65, 96, 448), ("widel_mt4_nt7_w4_d4_split1", 130, 224, 1088)]
+                ("wide_mt4_nt1_w8_d4_split3", 65, 96, 448), ("widel_mt4_nt7_w4_d4_split1", 130, 224, 1088),
+                # eight waves of eight steps: ragged rows and a half step at the end of K,
+                # and a K split whose second part starts on an odd step
+                ("mt1_nt1_wn1_wk8_kpw8_split1_pq", 5, 640, 1088), ("mt1_nt1_wn1_wk8_kpw8_split2_pq", 13, 224, 7488)]
 
 
 @pytest.mark.parametrize("sched,M,N,K", GEMM_Q_CASES)
