@@ -691,7 +691,10 @@ def floors(torch, steps, samples, names):
 
 # The split-1 schedules the phase probe instantiates with stamps, by probe
 # index: (workload, schedule name the library must pick for it).
-PHASE_PROBES = {"c2": (0, "mt1_nt2_wn1_wk4_kpw1_split1"), "c3": (1, "mt1_nt1_wn1_wk14_kpw4_split1_r8")}
+# workload: (probe entry `which`, schedule, m tiles, subtiles, column waves per workgroup)
+PHASE_PROBES = {"c1": (2, "mt1_nt2_wn1_wk4_kpw3_split1", 1, 2, 1), "c2": (0, "mt1_nt2_wn1_wk4_kpw1_split1", 1, 2, 1),
+                "c3": (1, "mt1_nt1_wn1_wk14_kpw4_split1_r8", 1, 1, 1),
+                "c4": (3, "mt1_nt2_wn4_wk4_kpw4_split1", 1, 2, 4)}
 PHASE_NAMES = ["loads_issued", "a_staged", "products_done", "c_stores_issued", "c_stores_complete"]
 
 
@@ -719,15 +722,14 @@ def phases(torch, mx, steps, names=("c2", "c3")):
     sh = stream.cuda_stream
     out = {}
     for name in names:
-        which, sched = PHASE_PROBES[name]
+        which, sched, mt, nt, wn = PHASE_PROBES[name]
         w = workload(name)
         M, N, K = w.M, w.N, w.K
         if mx.mxfp4_gemm_schedule_name(M, N, K) != sched:
             out[name] = {"skipped": "the library picks %s" % mx.mxfp4_gemm_schedule_name(M, N, K)}
             continue
         waves = L.mxfp4_probe_phases_waves(which)
-        nt = 2 if which == 0 else 1  # both schedules have one 16-row m tile and one column wave
-        grid = (N // (16 * nt)) * ((M + 15) // 16)
+        grid = (N // (16 * nt * wn)) * ((M + 16 * mt - 1) // (16 * mt))
         words = grid * waves * 8
         sets, graphs = rotation(set_bytes(M, N, K), steps)
         bufs = prepare(torch, mx, w, sets)

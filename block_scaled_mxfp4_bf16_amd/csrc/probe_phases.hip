@@ -1,12 +1,15 @@
 // Phase-timing probe of the fused small-M kernel (libmxfp4_probes.so; used by
 // bench.py --floors only).  It instantiates the fused kernel with its STAMPS
-// flag on for two split-1 schedules, built with the same flags as the
+// flag on for four split-1 schedules, built with the same flags as the
 // library's own instantiations, so the code between the stamps is the
 // library's:
 //   which 0: 1 m tile x 2 subtiles x 1 column wave x 4 K waves x 1 step
 //            (the schedule of 32 x 4096 x 512);
 //   which 1: the same with 1 subtile, 14 K waves of 4 steps, 8-row A blocks
-//            (the schedule of 8 x 2112 x 7168).
+//            (the schedule of 8 x 2112 x 7168);
+//   which 2: 2 subtiles, 4 K waves of 3 steps (16 x 3072 x 1536);
+//   which 3: 2 subtiles x 4 column waves, 4 K waves of 4 steps
+//            (64 x 7168 x 2048).
 // Each wave writes six 100 MHz real-time stamps (entry, loads issued, A
 // staged, products done, C stores issued, C stores complete) at
 // stamps[(workgroup * waves + wave) * 8 + i]; C is written as by the library.
@@ -52,13 +55,17 @@ __attribute__((visibility("default"))) int mxfp4_probe_phases(int which, const v
                                                     (hipStream_t)stream);
     case 1: return launch_stamped<1, 1, 1, 14, 4, 8>(A, Bw, Bs, C, stamps, stamp_words, M, N, K, sw,
                                                     (hipStream_t)stream);
+    case 2: return launch_stamped<1, 2, 1, 4, 3, 16>(A, Bw, Bs, C, stamps, stamp_words, M, N, K, sw,
+                                                    (hipStream_t)stream);
+    case 3: return launch_stamped<1, 2, 4, 4, 4, 16>(A, Bw, Bs, C, stamps, stamp_words, M, N, K, sw,
+                                                    (hipStream_t)stream);
     default: return 2;
   }
 }
 
 // Waves per workgroup of schedule `which` (0 if unknown).
 __attribute__((visibility("default"))) int mxfp4_probe_phases_waves(int which) {
-  return which == 0 ? 4 : which == 1 ? 14 : 0;
+  return which == 0 ? 4 : which == 1 ? 14 : which == 2 ? 4 : which == 3 ? 16 : 0;
 }
 
 }  // extern "C"

@@ -23,7 +23,7 @@ def test_floor_probes_run_and_are_plausible():
         assert m["cycles_per_instruction_per_wave"] >= 15.5
 
 
-@pytest.mark.parametrize("name", ["c2", "c3"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
 def test_phase_probe_matches_library_and_stamps_are_ordered(name):
     """The stamped copy of the fused kernel writes the library's C bit for
     bit, and every wave's stamps come in phase order."""
