@@ -461,6 +461,37 @@ DEFAULT_SHAPES = [(1, 32, 64), (3, 96, 4160), (17, 288, 448), (48, 1024, 1024), 
                   (192, 2048, 4096), (129, 3584, 2048), (160, 4096, 2048)]
 
 
+def _random_shapes(n, seed=2026, max_mnk=1.5e9):
+    """Seeded shapes for the built-in choice off the tuned table: M 1-300, N a
+    multiple of 32 up to 4096, K a multiple of 64 up to 8192, small enough
+    for the oracle to finish in a fraction of a second each."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(rng.integers(1, 301))
+        N = 32 * int(rng.integers(1, 129))
+        K = 64 * int(rng.integers(1, 129))
+        if M * N * K <= max_mnk:
+            out.append((M, N, K))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes(24)
+
+
+@pytest.mark.parametrize("M,N,K", RANDOM_SHAPES)
+def test_builtin_choice_on_random_shapes_matches_oracle(M, N, K):
+    """Whatever schedule the built-in choice picks (table, cost model, large-M
+    kernel), mxfp4_gemm and mxfp4_gemm_q match the oracle on every output."""
+    torch = torch_cuda()
+    c = make(torch, M, N, K, seed=M + 7 * N + 13 * K)
+    ref = c.ref()
+    assert_close(c.run(), ref, "gemm %dx%dx%d (%s)" % (M, N, K, mx.mxfp4_gemm_schedule_name(M, N, K)))
+    aq, as_ = mx.quantize(c.A, shuffled_scales=True)
+    got_q = bf16_dev_to_bits(mx.gemm_q(aq, as_, c.Bw, c.Bs, N))
+    assert_close(got_q, ref, "gemm_q %dx%dx%d (%s)" % (M, N, K, mx.mxfp4_gemm_q_schedule_name(M, N, K)))
+
+
 @pytest.mark.parametrize("M,N,K", DEFAULT_SHAPES)
 def test_default_schedules_match_oracle(M, N, K):
     torch = torch_cuda()
