@@ -423,6 +423,57 @@ def time_prepare_b(torch, mx, w, steps=50):
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "buffer_sets": sets}
 
 
+def time_quantize(torch, mx, w, shuffled, steps=50, samples=5, min_bytes=COLD_BYTES):
+    """The standalone quantization (mxfp4_quantize) of a workload's A, raw or
+    with shuffled scales, cold: the calls cycle in order through copies of A
+    in one buffer of >= 1 GiB (several graphs of `steps` calls cover them
+    all), median over `samples` replays of the whole rotation.  Bytes: bf16 A
+    read, codes and scales written."""
+    import numpy as np
+    M, K = w.M, w.K
+    a = torch.from_numpy(w.a_bits().view(np.int16)).view(torch.bfloat16).to("cuda")
+    sets, graphs = rotation(2 * M * K, steps, min_bytes)
+    big = torch.empty((sets, M, K), dtype=torch.bfloat16, device="cuda")
+    big.copy_(a.unsqueeze(0).expand(sets, M, K))
+    q = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+    s_bytes = mx.mxfp4_shuffled_scale_bytes(M, K) if shuffled else M * (K // 32)
+    sc = torch.empty(s_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            mx.mxfp4_quantize(big[i], M, K, q, sc, shuffled, stream=stream)
+    stream.synchronize()
+    gs = []
+    for j in range(graphs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                mx.mxfp4_quantize(big[j * steps + i], M, K, q, sc, shuffled, stream=stream)
+        gs.append(g)
+    with torch.cuda.stream(stream):
+        for g in gs:
+            g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(samples):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            for g in gs:
+                g.replay()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1) * 1e3 / sets)
+    us = percentile(times, 50)
+    nbytes = 2 * M * K + M * K // 2 + s_bytes
+    del gs, big
+    torch.cuda.empty_cache()
+    return {"M": M, "K": K, "scales": "shuffled" if shuffled else "raw", "us_per_call": round(us, 3), "bytes": nbytes,
+            "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "buffer_sets": sets}
+
+
 CPU_SAMPLE_ROWS = 8  # rows of the headline workload's A in the oracle's sample
 
 
@@ -930,7 +981,8 @@ def main():
     ap.add_argument("--configs", default="c1,c2,c3,c4,c5,p_4x2880x512,p_16x2112x7168,p_32x2880x512,p_256x3072x1536",
                     help="configurations measured under per_config (the headline is always measured)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-b-prep", action="store_true", help="skip timing the one-launch B preparation")
+    ap.add_argument("--no-b-prep", action="store_true",
+                    help="skip timing the one-launch B preparation and the standalone quantization of A")
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the second, warm timing (one buffer set, so inputs stay in L2 and MALL)")
     ap.add_argument("--no-clocks", action="store_true", help="skip reading the GPU clocks with amd-smi")
@@ -1033,6 +1085,17 @@ def main():
             print("[bench] B prep %dx%d: %.2f us, %.0f GB/s (%.1f%% of HBM)" % (w.N, w.K, r["us_per_call"], r["gbs"],
                                                                            100 * r["hbm_frac"]),
                   file=sys.stderr, flush=True)
+        # the standalone quantization of A (mxfp4_quantize), raw and with shuffled scales
+        line["quantize_a"] = {}
+        for name in ("c2", "c5"):
+            w = workload(name)
+            line["quantize_a"][w.name] = {}
+            for shuffled in (False, True):
+                r = time_quantize(torch, mx, w, shuffled)
+                line["quantize_a"][w.name][r["scales"]] = r
+                print("[bench] quantize A %dx%d (%s scales): %.2f us, %.0f GB/s (%.1f%% of HBM)"
+                      % (w.M, w.K, r["scales"], r["us_per_call"], r["gbs"], 100 * r["hbm_frac"]), file=sys.stderr,
+                      flush=True)
     if not args.no_clocks:
         line["clocks"] = {"before": clocks_before, "under_headline_load": h.get("clocks_under_load"),
                           "after": gpu_clocks()}

@@ -51,3 +51,15 @@ def test_wide_phase_probe_matches_library_and_stamps_are_ordered():
         assert out["workgroup_phase_us"][ph]["median"] >= 0.0
     assert 0.0 < out["first_entry_to_last_completion_us"]["median"] < 1000.0
     assert len(out["median_completion_by_xcd_us"]) >= 1
+
+
+@pytest.mark.parametrize("shuffled", [False, True])
+def test_quantize_timing_runs_and_is_plausible(shuffled):
+    """The bench's timing of the standalone quantization of A: a positive
+    time, and no faster than HBM's peak allows for the bytes it moves."""
+    torch = torch_cuda()
+    import block_scaled_mxfp4_bf16_amd as mx
+    r = bench.time_quantize(torch, mx, bench.workload("c2"), shuffled, steps=8, samples=2, min_bytes=1 << 22)
+    assert r["us_per_call"] > 0
+    assert r["gbs"] < bench.HBM_PEAK_GBS * 1.05
+    assert r["scales"] == ("shuffled" if shuffled else "raw")
