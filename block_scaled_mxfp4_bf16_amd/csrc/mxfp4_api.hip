@@ -83,7 +83,7 @@ const Tuned kTuned[] = {
     // the leaderboard's other shapes
     {4, 2880, 512, "mt1_nt2_wn1_wk4_kpw1_split1"},
     {16, 2112, 7168, "mt1_nt1_wn4_wk4_kpw4_split4"},
-    {32, 2880, 512, "mt1_nt1_wn4_wk1_kpw4_split1"},
+    {32, 2880, 512, "mt1_nt2_wn1_wk4_kpw1_split1"},
     {256, 3072, 1536, "mt2_nt2_wn3_wk4_kpw3_split1"},
     // A given quantized (mxfp4_gemm_q); the large-M entry above serves it too
     {16, 3072, 1536, "mt1_nt1_wn1_wk8_kpw2_split1_pq"},
